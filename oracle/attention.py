@@ -1,0 +1,78 @@
+"""Decode attention over K/V gathered through the block table, in fp64.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+The attention itself is ordinary softmax attention; the only difference from
+the contiguous case is that key and value rows are fetched from scattered
+physical blocks through the sequence's block table (page 3, section 06,
+misconception 1; page 1, section 3(3), step 2): the logical blocks look
+contiguous while the data is read from physical blocks; page 2, the
+architecture paragraph on the "forth" query vector reading keys and values
+from non-contiguous blocks).
+
+For sequence s with n = context_lens[s] tokens and query head h:
+
+  g       = h // G,  G = num_q_heads // num_kv_heads  (query heads h with equal
+            h // G share one KV head; the pages do not mention grouped heads,
+            this is the plain reading the grouped-head workloads need)
+  K_t     = k_cache[block_tables[s][t // B], g, t % B, :]   for t < n
+  V_t     = v_cache[block_tables[s][t // B], g, t % B, :]
+  l_t     = scale * <q[s, h, :], K_t>
+  out     = sum_t exp(l_t - max_u l_u) V_t / sum_t exp(l_t - max_u l_u)
+
+and out = 0 when n = 0.  Slots at positions >= n and blocks the table does not
+reach are never read, so whatever bits they hold (NaN included) cannot reach
+the result.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def to_f64(x, dtype: str):
+    """Exact up-cast to fp64: 'bf16' arrays are uint16 bit patterns, 'f32'
+    arrays are float32."""
+    x = np.asarray(x)
+    if dtype == "bf16":
+        if x.dtype != np.uint16:
+            raise TypeError("bf16 data must be given as uint16 bit patterns")
+        return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if dtype == "f32":
+        if x.dtype != np.float32:
+            raise TypeError("f32 data must be float32")
+        return x.astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens,
+                           scale: float, dtype: str, seqs=None, heads=None):
+    """fp64 decode attention.  Returns out[S, Hq, D] (fp64).
+
+    q: [S, Hq, D]; k_cache, v_cache: [NB, Hkv, B, D]; block_tables: [S, M];
+    context_lens: [S].  ``seqs`` / ``heads`` restrict the work to a subset
+    (the other rows of the result stay 0), for sampled checks at full size.
+    """
+    S, Hq, D = q.shape
+    _, Hkv, B, _ = k_cache.shape
+    if Hq % Hkv != 0:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    G = Hq // Hkv
+    out = np.zeros((S, Hq, D), dtype=np.float64)
+    seq_list = range(S) if seqs is None else seqs
+    head_list = range(Hq) if heads is None else heads
+    for s in seq_list:
+        n = int(context_lens[s])
+        if n == 0:
+            continue
+        blocks = [int(block_tables[s][t // B]) for t in range(n)]
+        offsets = [t % B for t in range(n)]
+        for h in head_list:
+            g = h // G
+            K = to_f64(k_cache[blocks, g, offsets, :], dtype)   # [n, D]
+            V = to_f64(v_cache[blocks, g, offsets, :], dtype)   # [n, D]
+            qh = to_f64(q[s, h, :], dtype)                      # [D]
+            logits = scale * (K @ qh)                           # [n]
+            w = np.exp(logits - logits.max())
+            out[s, h, :] = (w @ V) / w.sum()
+    return out
