@@ -1,0 +1,280 @@
+"""Benchmark of the paged-KV decode path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload 2] [--block-size B]
+
+One step is one pass of the whole hot path over one batch: the host allocator
+appends one token to every sequence (lazy allocation, copy-on-write pairs),
+then on the GPU copy_blocks (when the step produced pairs), paged_kv_write of
+the new tokens, and paged_attention_decode (partition + reduce).  The
+allocator's output for every step is computed before the timed region and
+uploaded, so the timed region starts with every input resident in HBM.
+
+Workloads (seeded synthetic inputs, see datagen):
+  2  64 seqs, 32 q / 8 kv heads, head_dim 128, bf16, block 16,
+     context U{128..4096}  (default; the headline configuration)
+  4  8 seqs x 32768 tokens, same heads
+  5  256 seqs, context log-uniform 16..8192, 64 q / 8 kv heads (--block-size)
+
+Prints one JSON line.  ``value`` = algorithmic KV bytes the decode reads per
+step / step time, in GB/s (1e9 B/s).  ``roofline`` reports the decode call
+alone, timed with HIP events on its stream.  ``cpu_baseline`` is the fp64
+oracle decoding the same step-0 batch on one host core.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+WORKLOAD_NAMES = {
+    2: "llama3-8b-layer decode: 64 seqs, 32 q / 8 kv heads, head_dim 128, bf16, block 16, "
+       "context U{128..4096}, pool 1.25x need, blocks scattered",
+    4: "long-context decode: 8 seqs x 32768 tokens, 32 q / 8 kv heads, head_dim 128, bf16, "
+       "block 16, partitions of 512",
+    5: "mixed decode + append: 256 seqs, context log-uniform 16..8192, 64 q / 8 kv heads, "
+       "head_dim 128, bf16",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, choices=[2, 4, 5])
+    ap.add_argument("--block-size", type=int, default=None)
+    ap.add_argument("--partition-size", type=int, default=512)
+    ap.add_argument("--replicas", type=int, default=1,
+                    help="rotate over R copies of the KV pool (step i uses copy i %% R)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class Workload:
+    """Host-side state of a workload: pools, allocator, per-step plans."""
+
+    def __init__(self, workload: int, block_size, steps_total: int, seed_extra: int = 0):
+        import datagen
+        import paged_kv_cache_377_amd as pkv
+
+        self.workload = workload
+        if workload == 5:
+            w = datagen.mixed_step_inputs(block_size or 16)
+            # the cache holds ctx - 1 tokens; the first step appends the last one
+            admitted = w.context_lens - 1
+        else:
+            w = datagen.decode_inputs(workload, block_size=block_size)
+            admitted = w.context_lens
+        self.w = w
+        sh = w.shape
+        self.shape = sh
+        B = sh.block_size
+        S = sh.num_seqs
+        # headroom for the tokens the timed steps append
+        grow = -(-steps_total // B) + 1
+        need = int(sum(-(-int(n) // B) for n in admitted)) + S * grow
+        nb = max(w.num_blocks, need)
+        order = w.free_order
+        if nb > w.num_blocks:
+            rng = np.random.default_rng(datagen.seed_for(workload) + 17)
+            order = np.concatenate([order, w.num_blocks + rng.permutation(nb - w.num_blocks)]).astype(np.int32)
+            extra_shape = (nb - w.num_blocks,) + w.k_cache.shape[1:]
+            w.k_cache = np.concatenate([w.k_cache, datagen.normal(rng, extra_shape, sh.dtype)])
+            w.v_cache = np.concatenate([w.v_cache, datagen.normal(rng, extra_shape, sh.dtype)])
+        self.num_blocks = nb
+        self.alloc = pkv.BlockAllocator(nb, B, order)
+        self.seq_ids = np.arange(S, dtype=np.int64)
+        prefix_slots = [self.alloc.add(int(s), int(admitted[s])) for s in range(S)]
+        if workload == 5:
+            # write the cached prefix into the pool (host side, before timing)
+            slots = np.concatenate(prefix_slots)
+            blk, off = slots // B, slots % B
+            w.k_cache[blk, :, off, :] = w.extra["prefix_k"]
+            w.v_cache[blk, :, off, :] = w.extra["prefix_v"]
+        self.width = -(-(int(admitted.max()) + steps_total) // B)
+        rng = np.random.default_rng(datagen.seed_for(workload) + 31 + seed_extra)
+        self.steps = []
+        for i in range(steps_total):
+            slots, pairs = self.alloc.step(self.seq_ids)
+            tables, ctx = self.alloc.build_tables(self.seq_ids, self.width)
+            if workload == 5 and i == 0:
+                nk, nv = w.extra["new_k"], w.extra["new_v"]
+            else:
+                nk = datagen.normal(rng, (S, sh.num_kv_heads, sh.head_dim), sh.dtype)
+                nv = datagen.normal(rng, (S, sh.num_kv_heads, sh.head_dim), sh.dtype)
+            q = w.q if i == 0 else datagen.normal(rng, w.q.shape, sh.dtype)
+            self.steps.append(dict(slots=slots, pairs=pairs, tables=tables, ctx=ctx, k=nk, v=nv, q=q))
+
+    def kv_bytes(self, i: int) -> int:
+        sh = self.shape
+        return int(self.steps[i]["ctx"].astype(np.int64).sum()) * sh.num_kv_heads * sh.head_dim * 2 * sh.elem_bytes
+
+    def algorithmic_bytes(self, i: int) -> int:
+        """K/V rows read + q read + out written + table entries read + lengths."""
+        sh = self.shape
+        st = self.steps[i]
+        blocks = int(sum(-(-int(n) // sh.block_size) for n in st["ctx"]))
+        qo = 2 * sh.num_seqs * sh.num_q_heads * sh.head_dim * sh.elem_bytes
+        return self.kv_bytes(i) + qo + 4 * blocks * sh.num_kv_heads + 4 * sh.num_seqs
+
+
+def to_dev(a, torch):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def cpu_baseline(wl: Workload, budget_s: float = 20.0):
+    """fp64 oracle on one host core, decoding step 0's batch."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    sh = wl.shape
+    st = wl.steps[0]
+    kc, vc = oracle.paged_kv_write(st["k"], st["v"], st["slots"], wl.w.k_cache, wl.w.v_cache)
+    seqs = []
+    t0 = time.perf_counter()
+    with threadpool_limits(1):
+        for s in range(sh.num_seqs):
+            oracle.paged_attention_decode(st["q"], kc, vc, st["tables"], st["ctx"], sh.scale,
+                                          sh.dtype, seqs=[s])
+            seqs.append(s)
+            if time.perf_counter() - t0 > budget_s:
+                break
+    dt = time.perf_counter() - t0
+    b = int(st["ctx"][seqs].astype(np.int64).sum()) * sh.num_kv_heads * sh.head_dim * 2 * sh.elem_bytes
+    return {"value": b / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 decode of {len(seqs)} of {sh.num_seqs} sequences (all "
+                      f"{sh.num_q_heads} heads) of step 0, {dt:.1f} s, numpy/BLAS limited to 1 thread",
+            "seqs_per_s": len(seqs) / dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import paged_kv_cache_377_amd as pkv
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    total = args.warmup + args.steps
+    t_setup = time.perf_counter()
+    wl = Workload(args.workload, args.block_size, total)
+    sh = wl.shape
+    print(f"[bench] workload {args.workload}: S={sh.num_seqs} NB={wl.num_blocks} "
+          f"ctx sum={int(wl.steps[0]['ctx'].sum())} setup {time.perf_counter() - t_setup:.1f}s",
+          file=sys.stderr, flush=True)
+
+    R = max(1, args.replicas)
+    kcs = [to_dev(wl.w.k_cache, torch) for _ in range(R)]
+    vcs = [to_dev(wl.w.v_cache, torch) for _ in range(R)]
+    dsteps = []
+    for st in wl.steps:
+        dsteps.append(dict(
+            slots=to_dev(st["slots"], torch), tables=to_dev(st["tables"], torch),
+            ctx=to_dev(st["ctx"], torch), k=to_dev(st["k"], torch), v=to_dev(st["v"], torch),
+            q=to_dev(st["q"], torch),
+            pairs=to_dev(st["pairs"], torch) if len(st["pairs"]) else None,
+            max_ctx=int(st["ctx"].max())))
+    out = torch.empty_like(dsteps[0]["q"])
+    ws_bytes = max(pkv.decode_workspace_bytes(sh.num_seqs, sh.num_q_heads, sh.head_dim, d["max_ctx"],
+                                              args.partition_size) for d in dsteps)
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(total)]
+    torch.cuda.synchronize()
+
+    def step(i):
+        d = dsteps[i]
+        kc, vc = kcs[i % R], vcs[i % R]
+        ev[i][0].record(stream)
+        if d["pairs"] is not None:
+            pkv.copy_blocks(kc, vc, d["pairs"], stream=stream)
+        pkv.paged_kv_write(d["k"], d["v"], d["slots"], kc, vc, stream=stream)
+        ev[i][1].record(stream)
+        pkv.paged_attention_decode(out, d["q"], kc, vc, d["tables"], d["ctx"], sh.scale,
+                                   d["max_ctx"], args.partition_size, workspace=workspace,
+                                   stream=stream)
+        ev[i][2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, total):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    timed = range(args.warmup, total)
+    step_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in timed]
+    dec_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in timed]
+    kv = sum(wl.kv_bytes(i) for i in timed)
+    alg = sum(wl.algorithmic_bytes(i) for i in timed)
+    ms_per_step = wall * 1e3 / args.steps
+    value = kv / (wall) / 1e9
+    dec_avg_ms = sum(dec_ms) / len(dec_ms)
+    achieved = alg / args.steps / (dec_avg_ms * 1e-3) / 1e9
+    res = {
+        "metric": "paged-decode KV-read GB/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": sh.dtype,
+        "data": "synthetic (seeded N(0,1) q/K/V, allocator-scattered blocks)",
+        "config": {"workload": WORKLOAD_NAMES[args.workload], "num_seqs": sh.num_seqs,
+                   "num_q_heads": sh.num_q_heads, "num_kv_heads": sh.num_kv_heads,
+                   "head_dim": sh.head_dim, "block_size": sh.block_size,
+                   "partition_size": args.partition_size, "pool_blocks": wl.num_blocks,
+                   "mean_context": float(np.mean([wl.steps[i]["ctx"].mean() for i in timed])),
+                   "replicas": R},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "decode_seqs_per_s": round(sh.num_seqs / (ms_per_step * 1e-3), 1),
+        "event_ms_per_step": round(sum(step_ms) / len(step_ms), 4),
+        "decode_ms": round(dec_avg_ms, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "paged_attention_decode (partition + reduce)",
+                     "algorithmic_bytes_per_launch": int(alg / args.steps)},
+        "allocator_us_per_step": None,
+    }
+    # host allocator cost per step (not in the timed GPU region)
+    import paged_kv_cache_377_amd as pkv2
+    a2 = pkv2.BlockAllocator(wl.num_blocks, sh.block_size)
+    for s in range(sh.num_seqs):
+        a2.add(s, int(wl.steps[0]["ctx"][s]) - 1)
+    t1 = time.perf_counter()
+    for _ in range(50):
+        a2.step(wl.seq_ids)
+        a2.build_tables(wl.seq_ids, wl.width + 8)
+    res["allocator_us_per_step"] = round((time.perf_counter() - t1) / 50 * 1e6, 1)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl)
+        res["cpu_baseline"]["value"] = round(res["cpu_baseline"]["value"], 4)
+        res["cpu_baseline"]["seqs_per_s"] = round(res["cpu_baseline"]["seqs_per_s"], 3)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

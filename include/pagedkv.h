@@ -1,0 +1,272 @@
+/*
+ * pagedkv.h -- C ABI of the MI355X (gfx950) paged KV-cache decode library.
+ *
+ * The KV cache is cut into fixed-size physical blocks; a sequence reaches its
+ * tokens through a block table that maps logical block i to a physical block
+ * (PagedAttention blog, 0539edu.com, section 3(3) "PagedAttention处理单个请求").
+ * This library provides the three device operations of that design and the
+ * host-side block allocator that feeds them:
+ *
+ *   pkv_paged_kv_write          write new tokens' K/V into their slots
+ *   pkv_copy_blocks             copy whole blocks (copy-on-write of shared blocks)
+ *   pkv_paged_attention_decode  one-query-per-sequence attention through the table
+ *   pkv_alloc_* / pkv_seq_*     free list, ref counts, lazy allocation, fork, CoW
+ *
+ * Conventions common to every call:
+ *   - Return value: PKV_OK (0) or a negative PKV_E* code.  Nothing is thrown
+ *     across the ABI.  On error no kernel is launched and allocator state is
+ *     unchanged; pkv_last_error() gives a message (thread-local).
+ *   - Device pointers are caller-owned device memory (the library never
+ *     allocates or frees device memory).  Host pointers are caller-owned host
+ *     memory.  `stream` is a hipStream_t passed as void* (NULL = null stream);
+ *     every device call is asynchronous on it and does no device->host sync.
+ *   - Cache layout (both K and V): [num_blocks, num_kv_heads, block_size,
+ *     head_dim], contiguous, element type `dtype`.  One (block, head) pair is
+ *     one contiguous run of block_size * head_dim elements.
+ *   - Compiled instances: dtype in {PKV_F32, PKV_BF16}, head_dim in {64, 128},
+ *     block_size in {8, 16, 32}, query heads per KV head in {1, 2, 4, 8}.
+ *     Other shapes return PKV_EUNSUPPORTED.
+ *   - The allocator is not thread-safe: one scheduler thread owns a handle.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  PKV_OK = 0,
+  PKV_EINVAL = -1,       /* bad shape, dtype, id or argument                  */
+  PKV_ENOBLOCKS = -2,    /* the pool cannot supply the blocks a call needs     */
+  PKV_ERANGE = -3,       /* a validate call found an out-of-contract value     */
+  PKV_EHIP = -4,         /* a HIP launch or runtime call failed                */
+  PKV_EUNSUPPORTED = -5  /* (dtype, head_dim, block_size, group) not compiled  */
+};
+
+enum { PKV_F32 = 0, PKV_BF16 = 1 };
+
+typedef struct {
+  int32_t num_blocks;    /* physical blocks in the pool                       */
+  int32_t num_kv_heads;
+  int32_t block_size;    /* tokens per block                                  */
+  int32_t head_dim;
+  int32_t dtype;         /* PKV_F32 or PKV_BF16                               */
+} pkv_cache_desc;
+
+/* ------------------------------------------------------------------------ */
+/* Device operations                                                         */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Write the K/V of `num_tokens` new tokens into the cache through their slots
+ * (blog section 3(3): prefill fills the prompt's K/V into the physical blocks,
+ * each decode step adds the new token's K/V to its block; weishuz.com Month 2
+ * section 03, reading (4): the worker hands the kernels `slot_mapping`).
+ *
+ *   k, v          device, [num_tokens, num_kv_heads, head_dim], dtype c->dtype
+ *   slot_mapping  device, [num_tokens] int64; token t goes to block
+ *                 slot / block_size, offset slot % block_size, every head.
+ *                 Slots outside [0, num_blocks * block_size) are skipped.
+ *                 Two tokens naming one slot is a caller error (the result
+ *                 is then unspecified; pkv_validate_write reports it).
+ *   k_cache, v_cache  device, cache layout, updated in place.
+ * num_tokens == 0 launches nothing.  Errors: PKV_EINVAL (null pointer,
+ * negative count, bad desc), PKV_EUNSUPPORTED, PKV_EHIP.
+ */
+int pkv_paged_kv_write(const void* k, const void* v, const int64_t* slot_mapping,
+                       int32_t num_tokens, void* k_cache, void* v_cache,
+                       const pkv_cache_desc* c, void* stream);
+
+/*
+ * Copy whole blocks, all heads, K and V: block dst takes block src's contents
+ * (blog section 4 "Parallel Sampling", step (2): the sample that writes into
+ * a shared block first gets its own copy of it).
+ *
+ *   src_dst_pairs  device, [num_pairs][2] int32 {src, dst}.  Contract: every
+ *                  id in [0, num_blocks), dsts distinct, no dst is also a src
+ *                  (so every read sees pre-call contents).  A src may repeat.
+ * Pairs outside [0, num_blocks) are skipped by the kernel; the other contract
+ * violations give unspecified contents (pkv_validate_copy reports them).
+ * num_pairs == 0 launches nothing.  Errors: PKV_EINVAL, PKV_EHIP.
+ */
+int pkv_copy_blocks(void* k_cache, void* v_cache, const pkv_cache_desc* c,
+                    const int32_t* src_dst_pairs, int32_t num_pairs, void* stream);
+
+/*
+ * Bytes of device workspace pkv_paged_attention_decode needs for these sizes
+ * (0 when every sequence fits one partition).  partition_size as below.
+ */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_context_len, int32_t partition_size);
+
+/*
+ * Decode attention: one query token per sequence against that sequence's
+ * cached K/V, read through its block table (blog section 3(3), step 2):
+ * attention is computed over the logically contiguous tokens while the data
+ * comes from physical blocks; weishuz.com Month 2, section 06: the kernel is
+ * ordinary attention whose only difference is gathering K and V from
+ * non-contiguous addresses; section 02: the block table lives in GPU memory
+ * and the lookup happens inside the kernel).
+ *
+ * For sequence s with n = context_lens[s] and query head h, G = num_q_heads /
+ * c->num_kv_heads, g = h / G:
+ *   K_t = k_cache[block_tables[s*max_blocks_per_seq + t/B], g, t%B, :], t < n
+ *   out[s,h,:] = sum_t softmax_t(scale * <q[s,h,:], K_t>) * V_t   (0 if n == 0)
+ * computed in fp32 from dtype inputs and rounded to dtype (bf16:
+ * round-to-nearest-even).
+ *
+ *   out           device, [num_seqs, num_q_heads, head_dim], dtype
+ *   q             device, [num_seqs, num_q_heads, head_dim], dtype
+ *   block_tables  device, [num_seqs, max_blocks_per_seq] int32; only the
+ *                 first ceil(context_lens[s] / block_size) entries of row s
+ *                 are read and each must be in [0, num_blocks)
+ *   context_lens  device, [num_seqs] int32, each in [0, max_context_len]; it
+ *                 counts the token just written by pkv_paged_kv_write
+ *   max_context_len  host int, bound on context_lens (sizes the launch)
+ *   partition_size   tokens per split-context partition: a multiple of
+ *                 block_size and of 64, or 0 for no split (one partition
+ *                 holds the whole context)
+ *   workspace     device, >= pkv_decode_workspace_bytes(...) bytes (may be
+ *                 NULL when that is 0); contents need no initialisation
+ * Slots at positions >= n and blocks the table does not reach are never read
+ * (any bits, NaN included, leave the result unchanged).  The result does not
+ * depend on physical block ids and is the same on every run (no atomics).
+ * Errors: PKV_EINVAL (null pointer, bad sizes, workspace too small, partition
+ * size not allowed), PKV_EUNSUPPORTED, PKV_EHIP.
+ */
+int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
+                               const void* v_cache, const pkv_cache_desc* c,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t max_context_len, float scale,
+                               int32_t partition_size, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Host-side contract checks (synchronous, for debugging; no GPU needed).    */
+/* Each takes HOST copies of the index arrays and returns PKV_OK, PKV_ERANGE */
+/* (message names the first offending index) or PKV_EINVAL (bad arguments). */
+/* ------------------------------------------------------------------------ */
+
+/* in-range slots are pairwise distinct */
+int pkv_validate_write(const int64_t* slot_mapping, int32_t num_tokens,
+                       const pkv_cache_desc* c);
+/* ids in range, dsts distinct, no dst is a src */
+int pkv_validate_copy(const int32_t* src_dst_pairs, int32_t num_pairs,
+                      const pkv_cache_desc* c);
+/* 0 <= ctx <= max_context_len, ceil(ctx/B) <= width, read entries in range */
+int pkv_validate_decode(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        const int32_t* context_lens, int32_t num_seqs,
+                        int32_t max_context_len, const pkv_cache_desc* c);
+
+/* ------------------------------------------------------------------------ */
+/* Host block allocator                                                      */
+/* ------------------------------------------------------------------------ */
+/*
+ * The pool keeps a FIFO free list and a reference count per physical block
+ * (weishuz.com Month 2, section 03 reading (2): the block pool's free list;
+ * section 04: ref_cnt).  Blocks are taken from the head of the free list and
+ * returned to its tail.  A new block is taken only when a token crosses into
+ * a block the sequence has not mapped yet (section 02, row "page fault": lazy
+ * allocation).  A token appended into a shared, partially filled last block
+ * first copies that block (blog section 4, step (2)).  Sequence ids are
+ * arbitrary int64 values chosen by the caller.
+ */
+
+typedef struct pkv_alloc pkv_alloc;
+
+typedef struct {
+  int32_t num_blocks;
+  int32_t num_free;
+  int32_t block_size;
+  int32_t num_seqs;
+  int64_t capacity_tokens;   /* num_blocks * block_size                        */
+  int64_t allocated_slots;   /* (num_blocks - num_free) * block_size            */
+  int64_t filled_slots;      /* filled slots of blocks in use, each block once  */
+  int64_t logical_tokens;    /* sum of sequence lengths (shared tokens repeat)  */
+  double utilization;        /* filled_slots / allocated_slots (0 if none)      */
+} pkv_stats;
+
+/*
+ * New pool of `num_blocks` blocks of `block_size` tokens.  free_order: host
+ * [num_blocks] permutation of 0..num_blocks-1 giving the free list from head
+ * to tail, or NULL for ascending ids.  Returns NULL on bad arguments or
+ * out of host memory (pkv_last_error() says which).  The handle is owned by
+ * the library: release it with pkv_alloc_destroy.
+ */
+pkv_alloc* pkv_alloc_create(int32_t num_blocks, int32_t block_size,
+                            const int32_t* free_order);
+void pkv_alloc_destroy(pkv_alloc* a);
+
+/*
+ * Admit sequence `seq` holding `num_tokens` tokens (its prompt): takes
+ * ceil(num_tokens / block_size) blocks (blog section 3(3), step 1)).  slots_out:
+ * host [num_tokens] or NULL; receives the slot of every position.
+ * Errors: PKV_EINVAL (seq exists, num_tokens < 0), PKV_ENOBLOCKS.
+ */
+int pkv_seq_add(pkv_alloc* a, int64_t seq, int32_t num_tokens, int64_t* slots_out);
+
+/* `child` starts as a copy of `parent`: same table and length, every block
+ * gains a reference (blog section 4, step (1)).  Errors: PKV_EINVAL. */
+int pkv_seq_fork(pkv_alloc* a, int64_t parent, int64_t child);
+
+/*
+ * Reserve the slot of one new token of `seq`.  cow_out (host [2], may be
+ * NULL) receives {src, dst} when the shared last block had to be copied
+ * first (the caller runs pkv_copy_blocks before writing the token), else
+ * {-1, -1}.  Errors: PKV_EINVAL, PKV_ENOBLOCKS.
+ */
+int pkv_seq_append(pkv_alloc* a, int64_t seq, int64_t* slot_out, int32_t cow_out[2]);
+
+/*
+ * One decode step: append one token to each of seqs[0..n-1], in array order.
+ * All-or-nothing: the blocks the whole step needs are counted first; if the
+ * pool has fewer, nothing changes and PKV_ENOBLOCKS is returned with the
+ * message "failed to allocate K blocks: F free of N total" (weishuz.com Month 2,
+ * section 07: such a message should state the pool size).
+ *   slots_out      host [n] int64
+ *   cow_pairs_out  host [n][2] int32 (at most one copy per sequence)
+ *   num_cow_out    host, number of pairs written
+ * Errors: PKV_EINVAL (unknown or repeated id, n < 0), PKV_ENOBLOCKS.
+ */
+int pkv_step_append(pkv_alloc* a, const int64_t* seqs, int32_t n, int64_t* slots_out,
+                    int32_t* cow_pairs_out, int32_t* num_cow_out);
+
+/* Release a sequence: its blocks are visited from the last to the first, and
+ * each one whose count reaches 0 goes to the free-list tail.  Errors: PKV_EINVAL. */
+int pkv_seq_free(pkv_alloc* a, int64_t seq);
+
+/* Length and block count of one sequence.  Errors: PKV_EINVAL. */
+int pkv_seq_info(const pkv_alloc* a, int64_t seq, int32_t* len_out, int32_t* num_blocks_out);
+
+/*
+ * Block tables for seqs[0..n-1]: tables_out host [n][width] int32 (entries
+ * past a sequence's last block are 0 and are never read by the decode),
+ * ctx_lens_out host [n] int32.  Errors: PKV_EINVAL (unknown id, a sequence
+ * holding more than `width` blocks).
+ */
+int pkv_build_tables(const pkv_alloc* a, const int64_t* seqs, int32_t n,
+                     int32_t* tables_out, int32_t width, int32_t* ctx_lens_out);
+
+/* Pool counters (weishuz.com Month 2, section 05: KV cache size and
+ * utilisation; section 07: free-block count). */
+int pkv_alloc_stats(const pkv_alloc* a, pkv_stats* out);
+
+/* Copy out the free list (head to tail) and the reference counts:
+ * free_fifo_out host [num_blocks] (first *num_free_out entries written),
+ * ref_cnt_out host [num_blocks]. */
+int pkv_alloc_export(const pkv_alloc* a, int32_t* free_fifo_out, int32_t* num_free_out,
+                     int32_t* ref_cnt_out);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

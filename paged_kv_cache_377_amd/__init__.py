@@ -1,0 +1,31 @@
+"""MI355X-native paged KV cache: decode attention, slot_mapping write, block
+copy and host block allocator, behind the C ABI of include/pagedkv.h.
+
+The Python layer is a thin ctypes binding over ``libpagedkv.so`` (built
+in-tree for gfx950 by ``python -m paged_kv_cache_377_amd.build``); it loads
+the library on first use and raises if it is missing.
+"""
+
+from ._lib import (  # noqa: F401
+    PKV_BF16,
+    PKV_EHIP,
+    PKV_EINVAL,
+    PKV_ENOBLOCKS,
+    PKV_ERANGE,
+    PKV_EUNSUPPORTED,
+    PKV_F32,
+    PKV_OK,
+    BlockAllocator,
+    CacheDesc,
+    PagedKVError,
+    cache_desc,
+    copy_blocks,
+    decode_workspace_bytes,
+    header_functions,
+    lib,
+    paged_attention_decode,
+    paged_kv_write,
+    validate_copy,
+    validate_decode,
+    validate_write,
+)

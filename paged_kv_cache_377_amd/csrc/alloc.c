@@ -1,0 +1,560 @@
+/*
+ * Host block allocator, error state and host-side contract checks.
+ *
+ * Plain C11, no HIP: it builds into the shared library with the kernels and,
+ * on its own, with gcc for CPU tests and sanitizer runs.
+ *
+ * The pool follows the pages' description of PagedAttention's memory manager:
+ *   - fixed-size physical blocks and a per-sequence block table mapping
+ *     logical to physical blocks, with a filled count per block (PagedAttention
+ *     blog, 0539edu.com, section 3(3), step 1) Prefill);
+ *   - a free list and a reference count per block (weishuz.com Month 2,
+ *     section 03 reading (2), section 04);
+ *   - lazy allocation: a block is taken when a token crosses into a block not
+ *     mapped yet (weishuz.com Month 2, section 02, row "page fault");
+ *   - sharing by fork and copy-on-write of a shared, partially filled block
+ *     on a divergent write (blog section 4, steps (1) and (2)).
+ * Where the pages are silent: the free list is a FIFO (take at the head,
+ * return at the tail), a finished sequence releases its blocks last-to-first,
+ * a batch step appends in array order and is all-or-nothing.
+ */
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "pkv_internal.h"
+
+/* ------------------------------------------------------------------ errors */
+
+static _Thread_local char g_err[512];
+
+int pkv__fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+void pkv__clear_error(void) { g_err[0] = '\0'; }
+
+const char* pkv_last_error(void) { return g_err; }
+
+int pkv__check_desc(const pkv_cache_desc* c) {
+  if (!c) return pkv__fail(PKV_EINVAL, "cache descriptor is NULL");
+  if (c->num_blocks <= 0 || c->num_kv_heads <= 0 || c->block_size <= 0 || c->head_dim <= 0)
+    return pkv__fail(PKV_EINVAL, "cache descriptor has a non-positive size "
+                     "(num_blocks=%d num_kv_heads=%d block_size=%d head_dim=%d)",
+                     c->num_blocks, c->num_kv_heads, c->block_size, c->head_dim);
+  if (c->dtype != PKV_F32 && c->dtype != PKV_BF16)
+    return pkv__fail(PKV_EINVAL, "unknown dtype %d", c->dtype);
+  return PKV_OK;
+}
+
+/* --------------------------------------------------------------- the pool */
+
+typedef struct {
+  int64_t id;
+  int32_t len;       /* tokens held                                       */
+  int32_t nblk;      /* blocks mapped = ceil(len / block_size)             */
+  int32_t cap;
+  int32_t* blocks;   /* block table, logical -> physical                   */
+  uint32_t stamp;    /* last batch step that named this sequence           */
+  uint8_t state;     /* 0 empty, 1 live, 2 deleted                         */
+} seq_entry;
+
+struct pkv_alloc {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t* fifo;     /* ring buffer of free ids, capacity num_blocks       */
+  int32_t head;
+  int32_t nfree;
+  int32_t* ref;
+  int32_t* touched;  /* scratch for a step's dry run, capacity num_blocks  */
+  seq_entry* tab;    /* open-addressing map seq id -> entry                */
+  size_t tcap;       /* power of two                                       */
+  size_t nlive;
+  size_t nused;      /* live + deleted                                     */
+  uint32_t step_no;
+};
+
+static uint64_t mix64(uint64_t x) {
+  x ^= x >> 33;
+  x *= 0xff51afd7ed558ccdULL;
+  x ^= x >> 33;
+  x *= 0xc4ceb9fe1a85ec53ULL;
+  x ^= x >> 33;
+  return x;
+}
+
+static seq_entry* find(const pkv_alloc* a, int64_t id) {
+  size_t mask = a->tcap - 1;
+  for (size_t i = (size_t)mix64((uint64_t)id) & mask;; i = (i + 1) & mask) {
+    seq_entry* e = &a->tab[i];
+    if (e->state == 0) return NULL;
+    if (e->state == 1 && e->id == id) return e;
+  }
+}
+
+static int rehash(pkv_alloc* a, size_t new_cap) {
+  seq_entry* t = (seq_entry*)calloc(new_cap, sizeof(seq_entry));
+  if (!t) return pkv__fail(PKV_EINVAL, "out of host memory");
+  size_t mask = new_cap - 1;
+  for (size_t i = 0; i < a->tcap; ++i) {
+    seq_entry* e = &a->tab[i];
+    if (e->state != 1) continue;
+    size_t j = (size_t)mix64((uint64_t)e->id) & mask;
+    while (t[j].state != 0) j = (j + 1) & mask;
+    t[j] = *e;
+  }
+  free(a->tab);
+  a->tab = t;
+  a->tcap = new_cap;
+  a->nused = a->nlive;
+  return PKV_OK;
+}
+
+/* Insert a fresh entry for `id` (must be absent). */
+static seq_entry* insert(pkv_alloc* a, int64_t id) {
+  if ((a->nused + 1) * 2 > a->tcap) {
+    size_t cap = a->tcap;
+    while ((a->nlive + 1) * 4 > cap) cap *= 2;
+    if (rehash(a, cap) != PKV_OK) return NULL;
+  }
+  size_t mask = a->tcap - 1;
+  size_t i = (size_t)mix64((uint64_t)id) & mask;
+  while (a->tab[i].state == 1) i = (i + 1) & mask;
+  seq_entry* e = &a->tab[i];
+  if (e->state == 0) a->nused++;
+  memset(e, 0, sizeof *e);
+  e->id = id;
+  e->state = 1;
+  a->nlive++;
+  return e;
+}
+
+static void erase(pkv_alloc* a, seq_entry* e) {
+  free(e->blocks);
+  e->blocks = NULL;
+  e->state = 2;
+  a->nlive--;
+}
+
+static int reserve_blocks(seq_entry* e, int32_t n) {
+  if (n <= e->cap) return PKV_OK;
+  int32_t cap = e->cap ? e->cap : 4;
+  while (cap < n) cap *= 2;
+  int32_t* b = (int32_t*)realloc(e->blocks, (size_t)cap * sizeof(int32_t));
+  if (!b) return pkv__fail(PKV_EINVAL, "out of host memory");
+  e->blocks = b;
+  e->cap = cap;
+  return PKV_OK;
+}
+
+static int32_t take_block(pkv_alloc* a) {
+  int32_t b = a->fifo[a->head];
+  a->head = (a->head + 1 == a->num_blocks) ? 0 : a->head + 1;
+  a->nfree--;
+  a->ref[b] = 1;
+  return b;
+}
+
+static void return_block(pkv_alloc* a, int32_t b) {
+  int64_t tail = (int64_t)a->head + a->nfree;
+  if (tail >= a->num_blocks) tail -= a->num_blocks;
+  a->fifo[tail] = b;
+  a->nfree++;
+}
+
+static int no_blocks(const pkv_alloc* a, int64_t needed) {
+  return pkv__fail(PKV_ENOBLOCKS, "failed to allocate %lld blocks: %d free of %d total",
+                   (long long)needed, a->nfree, a->num_blocks);
+}
+
+pkv_alloc* pkv_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order) {
+  pkv__clear_error();
+  if (num_blocks <= 0 || block_size <= 0) {
+    pkv__fail(PKV_EINVAL, "num_blocks (%d) and block_size (%d) must be positive",
+              num_blocks, block_size);
+    return NULL;
+  }
+  pkv_alloc* a = (pkv_alloc*)calloc(1, sizeof *a);
+  if (!a) goto oom;
+  a->num_blocks = num_blocks;
+  a->block_size = block_size;
+  a->fifo = (int32_t*)malloc((size_t)num_blocks * sizeof(int32_t));
+  a->ref = (int32_t*)calloc((size_t)num_blocks, sizeof(int32_t));
+  a->touched = (int32_t*)malloc((size_t)num_blocks * sizeof(int32_t));
+  a->tcap = 64;
+  a->tab = (seq_entry*)calloc(a->tcap, sizeof(seq_entry));
+  if (!a->fifo || !a->ref || !a->touched || !a->tab) goto oom;
+  if (free_order) {
+    /* must be a permutation: use ref[] as a seen-mark, then clear it */
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      int32_t b = free_order[i];
+      if (b < 0 || b >= num_blocks || a->ref[b]) {
+        pkv__fail(PKV_EINVAL, "free_order is not a permutation of 0..%d (entry %d = %d)",
+                  num_blocks - 1, i, b);
+        pkv_alloc_destroy(a);
+        return NULL;
+      }
+      a->ref[b] = 1;
+      a->fifo[i] = b;
+    }
+    memset(a->ref, 0, (size_t)num_blocks * sizeof(int32_t));
+  } else {
+    for (int32_t i = 0; i < num_blocks; ++i) a->fifo[i] = i;
+  }
+  a->head = 0;
+  a->nfree = num_blocks;
+  return a;
+oom:
+  pkv__fail(PKV_EINVAL, "out of host memory");
+  pkv_alloc_destroy(a);
+  return NULL;
+}
+
+void pkv_alloc_destroy(pkv_alloc* a) {
+  if (!a) return;
+  if (a->tab)
+    for (size_t i = 0; i < a->tcap; ++i)
+      if (a->tab[i].state == 1) free(a->tab[i].blocks);
+  free(a->tab);
+  free(a->fifo);
+  free(a->ref);
+  free(a->touched);
+  free(a);
+}
+
+static int64_t slot_of(const pkv_alloc* a, const seq_entry* e, int32_t pos) {
+  int32_t B = a->block_size;
+  return (int64_t)e->blocks[pos / B] * B + pos % B;
+}
+
+int pkv_seq_add(pkv_alloc* a, int64_t seq, int32_t num_tokens, int64_t* slots_out) {
+  pkv__clear_error();
+  if (!a) return pkv__fail(PKV_EINVAL, "allocator handle is NULL");
+  if (num_tokens < 0) return pkv__fail(PKV_EINVAL, "num_tokens %d < 0", num_tokens);
+  if (find(a, seq)) return pkv__fail(PKV_EINVAL, "sequence %lld already exists", (long long)seq);
+  int32_t B = a->block_size;
+  int32_t need = (int32_t)(((int64_t)num_tokens + B - 1) / B);
+  if (need > a->nfree) return no_blocks(a, need);
+  seq_entry* e = insert(a, seq);
+  if (!e) return PKV_EINVAL;
+  if (reserve_blocks(e, need) != PKV_OK) {
+    erase(a, e);
+    return PKV_EINVAL;
+  }
+  for (int32_t i = 0; i < need; ++i) e->blocks[i] = take_block(a);
+  e->nblk = need;
+  e->len = num_tokens;
+  if (slots_out)
+    for (int32_t p = 0; p < num_tokens; ++p) slots_out[p] = slot_of(a, e, p);
+  return PKV_OK;
+}
+
+int pkv_seq_fork(pkv_alloc* a, int64_t parent, int64_t child) {
+  pkv__clear_error();
+  if (!a) return pkv__fail(PKV_EINVAL, "allocator handle is NULL");
+  seq_entry* p = find(a, parent);
+  if (!p) return pkv__fail(PKV_EINVAL, "unknown parent sequence %lld", (long long)parent);
+  if (find(a, child)) return pkv__fail(PKV_EINVAL, "sequence %lld already exists", (long long)child);
+  /* insert may move the table: remember the parent's contents by id */
+  seq_entry* c = insert(a, child);
+  if (!c) return PKV_EINVAL;
+  p = find(a, parent);
+  if (reserve_blocks(c, p->nblk) != PKV_OK) {
+    erase(a, c);
+    return PKV_EINVAL;
+  }
+  if (p->nblk) memcpy(c->blocks, p->blocks, (size_t)p->nblk * sizeof(int32_t));
+  c->nblk = p->nblk;
+  c->len = p->len;
+  for (int32_t i = 0; i < p->nblk; ++i) a->ref[p->blocks[i]]++;
+  return PKV_OK;
+}
+
+/* Blocks one append to `e` takes (0 or 1) given the current counts. */
+static int append_needs(const pkv_alloc* a, const seq_entry* e) {
+  int32_t pos = e->len, B = a->block_size;
+  if (pos % B == 0) return 1;
+  return a->ref[e->blocks[pos / B]] > 1;
+}
+
+/* Append one token; the caller has checked that a block is available when
+ * append_needs() says so.  Writes the slot and the copy pair (or -1, -1). */
+static int append_one(pkv_alloc* a, seq_entry* e, int64_t* slot_out, int32_t* cow) {
+  int32_t pos = e->len, B = a->block_size;
+  cow[0] = -1;
+  cow[1] = -1;
+  if (pos % B == 0) {
+    if (reserve_blocks(e, e->nblk + 1) != PKV_OK) return PKV_EINVAL;
+    e->blocks[e->nblk++] = take_block(a);
+  } else {
+    int32_t last = e->blocks[pos / B];
+    if (a->ref[last] > 1) {
+      int32_t fresh = take_block(a);
+      a->ref[last]--;
+      e->blocks[pos / B] = fresh;
+      cow[0] = last;
+      cow[1] = fresh;
+    }
+  }
+  *slot_out = slot_of(a, e, pos);
+  e->len = pos + 1;
+  return PKV_OK;
+}
+
+int pkv_seq_append(pkv_alloc* a, int64_t seq, int64_t* slot_out, int32_t cow_out[2]) {
+  pkv__clear_error();
+  if (!a) return pkv__fail(PKV_EINVAL, "allocator handle is NULL");
+  if (!slot_out) return pkv__fail(PKV_EINVAL, "slot_out is NULL");
+  seq_entry* e = find(a, seq);
+  if (!e) return pkv__fail(PKV_EINVAL, "unknown sequence %lld", (long long)seq);
+  if (e->len == INT32_MAX) return pkv__fail(PKV_EINVAL, "sequence %lld is full", (long long)seq);
+  if (append_needs(a, e) > a->nfree) return no_blocks(a, 1);
+  if (e->len % a->block_size == 0 && reserve_blocks(e, e->nblk + 1) != PKV_OK) return PKV_EINVAL;
+  int32_t cow[2];
+  int rc = append_one(a, e, slot_out, cow);
+  if (rc == PKV_OK && cow_out) {
+    cow_out[0] = cow[0];
+    cow_out[1] = cow[1];
+  }
+  return rc;
+}
+
+int pkv_step_append(pkv_alloc* a, const int64_t* seqs, int32_t n, int64_t* slots_out,
+                    int32_t* cow_pairs_out, int32_t* num_cow_out) {
+  pkv__clear_error();
+  if (!a) return pkv__fail(PKV_EINVAL, "allocator handle is NULL");
+  if (n < 0) return pkv__fail(PKV_EINVAL, "n %d < 0", n);
+  if (n > 0 && (!seqs || !slots_out || !cow_pairs_out))
+    return pkv__fail(PKV_EINVAL, "NULL array argument");
+  uint32_t stamp = ++a->step_no;
+  if (stamp == 0) { /* wrapped: clear every stamp once */
+    for (size_t i = 0; i < a->tcap; ++i) a->tab[i].stamp = 0;
+    stamp = a->step_no = 1;
+  }
+  /* pass 1: ids known and distinct; room in every table */
+  for (int32_t i = 0; i < n; ++i) {
+    seq_entry* e = find(a, seqs[i]);
+    if (!e || e->stamp == stamp)
+      return pkv__fail(PKV_EINVAL, "step names an unknown or repeated sequence (%lld at %d)",
+                       (long long)seqs[i], i);
+    e->stamp = stamp;
+    if (e->len == INT32_MAX) return pkv__fail(PKV_EINVAL, "sequence %lld is full", (long long)seqs[i]);
+    if (e->len % a->block_size == 0 && reserve_blocks(e, e->nblk + 1) != PKV_OK) return PKV_EINVAL;
+  }
+  /* pass 2: count blocks, lowering the count of each shared block a copy
+   * leaves, then undo those decrements */
+  int64_t needed = 0;
+  int32_t ntouched = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    seq_entry* e = find(a, seqs[i]);
+    int32_t pos = e->len, B = a->block_size;
+    if (pos % B == 0) {
+      needed++;
+    } else {
+      int32_t last = e->blocks[pos / B];
+      if (a->ref[last] > 1) {
+        needed++;
+        a->ref[last]--;
+        a->touched[ntouched++] = last;
+      }
+    }
+  }
+  for (int32_t i = 0; i < ntouched; ++i) a->ref[a->touched[i]]++;
+  if (needed > a->nfree) return no_blocks(a, needed);
+  /* pass 3: apply */
+  int32_t ncow = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    seq_entry* e = find(a, seqs[i]);
+    int32_t cow[2];
+    append_one(a, e, &slots_out[i], cow);
+    if (cow[0] >= 0) {
+      cow_pairs_out[2 * ncow] = cow[0];
+      cow_pairs_out[2 * ncow + 1] = cow[1];
+      ncow++;
+    }
+  }
+  if (num_cow_out) *num_cow_out = ncow;
+  return PKV_OK;
+}
+
+int pkv_seq_free(pkv_alloc* a, int64_t seq) {
+  pkv__clear_error();
+  if (!a) return pkv__fail(PKV_EINVAL, "allocator handle is NULL");
+  seq_entry* e = find(a, seq);
+  if (!e) return pkv__fail(PKV_EINVAL, "unknown sequence %lld", (long long)seq);
+  for (int32_t i = e->nblk - 1; i >= 0; --i) {
+    int32_t b = e->blocks[i];
+    if (--a->ref[b] == 0) return_block(a, b);
+  }
+  erase(a, e);
+  return PKV_OK;
+}
+
+int pkv_seq_info(const pkv_alloc* a, int64_t seq, int32_t* len_out, int32_t* num_blocks_out) {
+  pkv__clear_error();
+  if (!a) return pkv__fail(PKV_EINVAL, "allocator handle is NULL");
+  const seq_entry* e = find(a, seq);
+  if (!e) return pkv__fail(PKV_EINVAL, "unknown sequence %lld", (long long)seq);
+  if (len_out) *len_out = e->len;
+  if (num_blocks_out) *num_blocks_out = e->nblk;
+  return PKV_OK;
+}
+
+int pkv_build_tables(const pkv_alloc* a, const int64_t* seqs, int32_t n, int32_t* tables_out,
+                     int32_t width, int32_t* ctx_lens_out) {
+  pkv__clear_error();
+  if (!a) return pkv__fail(PKV_EINVAL, "allocator handle is NULL");
+  if (n < 0 || width < 0) return pkv__fail(PKV_EINVAL, "negative size (n=%d width=%d)", n, width);
+  if (n > 0 && (!seqs || !tables_out || !ctx_lens_out))
+    return pkv__fail(PKV_EINVAL, "NULL array argument");
+  for (int32_t i = 0; i < n; ++i) {
+    const seq_entry* e = find(a, seqs[i]);
+    if (!e) return pkv__fail(PKV_EINVAL, "unknown sequence %lld", (long long)seqs[i]);
+    if (e->nblk > width)
+      return pkv__fail(PKV_EINVAL, "sequence %lld holds %d blocks, more than width %d",
+                       (long long)seqs[i], e->nblk, width);
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const seq_entry* e = find(a, seqs[i]);
+    int32_t* row = tables_out + (size_t)i * (size_t)width;
+    if (e->nblk) memcpy(row, e->blocks, (size_t)e->nblk * sizeof(int32_t));
+    for (int32_t j = e->nblk; j < width; ++j) row[j] = 0;
+    ctx_lens_out[i] = e->len;
+  }
+  return PKV_OK;
+}
+
+int pkv_alloc_stats(const pkv_alloc* a, pkv_stats* out) {
+  pkv__clear_error();
+  if (!a || !out) return pkv__fail(PKV_EINVAL, "NULL argument");
+  int32_t B = a->block_size;
+  int32_t* fill = (int32_t*)calloc((size_t)a->num_blocks, sizeof(int32_t));
+  if (!fill) return pkv__fail(PKV_EINVAL, "out of host memory");
+  int64_t logical = 0;
+  for (size_t i = 0; i < a->tcap; ++i) {
+    const seq_entry* e = &a->tab[i];
+    if (e->state != 1) continue;
+    logical += e->len;
+    for (int32_t j = 0; j < e->nblk; ++j) {
+      int32_t f = e->len - j * B;
+      if (f > B) f = B;
+      if (f > fill[e->blocks[j]]) fill[e->blocks[j]] = f;
+    }
+  }
+  int64_t filled = 0;
+  for (int32_t b = 0; b < a->num_blocks; ++b) filled += fill[b];
+  free(fill);
+  out->num_blocks = a->num_blocks;
+  out->num_free = a->nfree;
+  out->block_size = B;
+  out->num_seqs = (int32_t)a->nlive;
+  out->capacity_tokens = (int64_t)a->num_blocks * B;
+  out->allocated_slots = (int64_t)(a->num_blocks - a->nfree) * B;
+  out->filled_slots = filled;
+  out->logical_tokens = logical;
+  out->utilization = out->allocated_slots ? (double)filled / (double)out->allocated_slots : 0.0;
+  return PKV_OK;
+}
+
+int pkv_alloc_export(const pkv_alloc* a, int32_t* free_fifo_out, int32_t* num_free_out,
+                     int32_t* ref_cnt_out) {
+  pkv__clear_error();
+  if (!a) return pkv__fail(PKV_EINVAL, "allocator handle is NULL");
+  if (free_fifo_out)
+    for (int32_t i = 0; i < a->nfree; ++i) {
+      int64_t j = (int64_t)a->head + i;
+      if (j >= a->num_blocks) j -= a->num_blocks;
+      free_fifo_out[i] = a->fifo[j];
+    }
+  if (num_free_out) *num_free_out = a->nfree;
+  if (ref_cnt_out) memcpy(ref_cnt_out, a->ref, (size_t)a->num_blocks * sizeof(int32_t));
+  return PKV_OK;
+}
+
+/* ------------------------------------------------------ contract checks */
+
+int pkv_validate_write(const int64_t* slot_mapping, int32_t num_tokens, const pkv_cache_desc* c) {
+  pkv__clear_error();
+  int rc = pkv__check_desc(c);
+  if (rc) return rc;
+  if (num_tokens < 0 || (num_tokens > 0 && !slot_mapping))
+    return pkv__fail(PKV_EINVAL, "bad slot_mapping argument");
+  int64_t nslots = (int64_t)c->num_blocks * c->block_size;
+  uint8_t* seen = (uint8_t*)calloc((size_t)nslots, 1);
+  if (!seen) return pkv__fail(PKV_EINVAL, "out of host memory");
+  for (int32_t t = 0; t < num_tokens; ++t) {
+    int64_t s = slot_mapping[t];
+    if (s < 0 || s >= nslots) continue;
+    if (seen[s]) {
+      free(seen);
+      return pkv__fail(PKV_ERANGE, "slot %lld of token %d is also named by an earlier token",
+                       (long long)s, t);
+    }
+    seen[s] = 1;
+  }
+  free(seen);
+  return PKV_OK;
+}
+
+int pkv_validate_copy(const int32_t* pairs, int32_t num_pairs, const pkv_cache_desc* c) {
+  pkv__clear_error();
+  int rc = pkv__check_desc(c);
+  if (rc) return rc;
+  if (num_pairs < 0 || (num_pairs > 0 && !pairs))
+    return pkv__fail(PKV_EINVAL, "bad pairs argument");
+  uint8_t* role = (uint8_t*)calloc((size_t)c->num_blocks, 1); /* bit0 src, bit1 dst */
+  if (!role) return pkv__fail(PKV_EINVAL, "out of host memory");
+  for (int32_t i = 0; i < num_pairs; ++i) {
+    int32_t s = pairs[2 * i], d = pairs[2 * i + 1];
+    if (s < 0 || s >= c->num_blocks || d < 0 || d >= c->num_blocks) {
+      free(role);
+      return pkv__fail(PKV_ERANGE, "pair %d (%d, %d) is outside [0, %d)", i, s, d, c->num_blocks);
+    }
+    role[s] |= 1;
+  }
+  for (int32_t i = 0; i < num_pairs; ++i) {
+    int32_t d = pairs[2 * i + 1];
+    if (role[d] & 1) {
+      free(role);
+      return pkv__fail(PKV_ERANGE, "pair %d: destination %d is also a source", i, d);
+    }
+    if (role[d] & 2) {
+      free(role);
+      return pkv__fail(PKV_ERANGE, "pair %d: destination %d repeats", i, d);
+    }
+    role[d] |= 2;
+  }
+  free(role);
+  return PKV_OK;
+}
+
+int pkv_validate_decode(const int32_t* block_tables, int32_t width, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t max_context_len, const pkv_cache_desc* c) {
+  pkv__clear_error();
+  int rc = pkv__check_desc(c);
+  if (rc) return rc;
+  if (num_seqs < 0 || width < 0 || (num_seqs > 0 && (!block_tables || !context_lens)))
+    return pkv__fail(PKV_EINVAL, "bad table arguments");
+  int32_t B = c->block_size;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    int32_t n = context_lens[s];
+    if (n < 0 || n > max_context_len)
+      return pkv__fail(PKV_ERANGE, "context_lens[%d] = %d is outside [0, %d]", s, n, max_context_len);
+    int32_t nb = (int32_t)(((int64_t)n + B - 1) / B);
+    if (nb > width)
+      return pkv__fail(PKV_ERANGE, "sequence %d needs %d table entries, width is %d", s, nb, width);
+    for (int32_t i = 0; i < nb; ++i) {
+      int32_t b = block_tables[(size_t)s * (size_t)width + i];
+      if (b < 0 || b >= c->num_blocks)
+        return pkv__fail(PKV_ERANGE, "block_tables[%d][%d] = %d is outside [0, %d)", s, i, b,
+                         c->num_blocks);
+    }
+  }
+  return PKV_OK;
+}

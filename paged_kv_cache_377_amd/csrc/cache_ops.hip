@@ -1,0 +1,148 @@
+// slot_mapping write and block copy for gfx950.
+//
+// Both kernels move bits, never values: every (token, head) row and every
+// (block, head) run is copied in 16-byte pieces (global_load/store_dwordx4),
+// so one wave moves a contiguous 1 KiB and the element type does not matter.
+//
+//  * Write (PagedAttention blog, 0539edu.com, section 3(3): the prompt's K/V
+//    are filled into the physical blocks, and each decode step adds the new
+//    token's K/V to its block; weishuz.com Month 2, section 03, reading (4):
+//    the worker passes `slot_mapping` to the kernels).  Token t, head h goes
+//    to block slot/B, offset slot%B.  Slots outside the pool are skipped.
+//  * Copy (blog section 4, step (2): a sample writing into a shared block
+//    first gets its own copy of it).  Block dst, all heads, K and V, takes
+//    block src's contents.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "pkv_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// One thread per 16-byte piece of the [T, Hkv, D] input.  `row_chunks` is
+// D * elem_bytes / 16 and `rows` = T * Hkv.
+__global__ __launch_bounds__(kThreads) void kv_write_kernel(
+    const uint4* __restrict__ k, const uint4* __restrict__ v,
+    const int64_t* __restrict__ slot_mapping, uint4* __restrict__ k_cache,
+    uint4* __restrict__ v_cache, int32_t num_kv_heads, int32_t block_size,
+    int32_t row_chunks, int64_t total_chunks, int64_t num_slots) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= total_chunks) return;
+  const int32_t c = (int32_t)(i % row_chunks);
+  const int64_t row = i / row_chunks;
+  const int32_t h = (int32_t)(row % num_kv_heads);
+  const int64_t t = row / num_kv_heads;
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / block_size;
+  const int64_t off = slot - blk * block_size;
+  const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * row_chunks + c;
+  const uint4 kv = k[i];
+  const uint4 vv = v[i];
+  k_cache[dst] = kv;
+  v_cache[dst] = vv;
+}
+
+// Grid: num_pairs * groups_per_block workgroups; each workgroup copies
+// kThreads * kPerThread pieces of one block's K and V run.
+constexpr int kPerThread = 4;
+
+__global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
+    uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
+    const int32_t* __restrict__ pairs, int32_t block_chunks, int32_t groups_per_block,
+    int32_t num_blocks) {
+  const int32_t pair = blockIdx.x / groups_per_block;
+  const int32_t grp = blockIdx.x - pair * groups_per_block;
+  const int32_t src = pairs[2 * pair];
+  const int32_t dst = pairs[2 * pair + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  const uint4* ks = k_cache + (int64_t)src * block_chunks;
+  const uint4* vs = v_cache + (int64_t)src * block_chunks;
+  uint4* kd = k_cache + (int64_t)dst * block_chunks;
+  uint4* vd = v_cache + (int64_t)dst * block_chunks;
+  const int32_t base = grp * (kThreads * kPerThread) + threadIdx.x;
+  uint4 kr[kPerThread], vr[kPerThread];
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const int32_t c = base + j * kThreads;
+    if (c < block_chunks) {
+      kr[j] = ks[c];
+      vr[j] = vs[c];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const int32_t c = base + j * kThreads;
+    if (c < block_chunks) {
+      kd[c] = kr[j];
+      vd[c] = vr[j];
+    }
+  }
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int elem_bytes(int32_t dtype) { return dtype == PKV_BF16 ? 2 : 4; }
+
+}  // namespace
+
+extern "C" int pkv_paged_kv_write(const void* k, const void* v, const int64_t* slot_mapping,
+                                  int32_t num_tokens, void* k_cache, void* v_cache,
+                                  const pkv_cache_desc* c, void* stream) {
+  pkv__clear_error();
+  int rc = pkv__check_desc(c);
+  if (rc) return rc;
+  if (num_tokens < 0) return pkv__fail(PKV_EINVAL, "num_tokens %d < 0", num_tokens);
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache)
+    return pkv__fail(PKV_EINVAL, "NULL device pointer");
+  const int64_t row_bytes = (int64_t)c->head_dim * elem_bytes(c->dtype);
+  if (row_bytes % 16 != 0)
+    return pkv__fail(PKV_EUNSUPPORTED, "head_dim * element size (%lld B) is not a multiple of 16",
+                     (long long)row_bytes);
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      ((uintptr_t)slot_mapping & 7u))
+    return pkv__fail(PKV_EINVAL, "device pointers must be 16-byte aligned (slot_mapping 8-byte)");
+  const int32_t row_chunks = (int32_t)(row_bytes / 16);
+  const int64_t total = (int64_t)num_tokens * c->num_kv_heads * row_chunks;
+  const int64_t grid = (total + kThreads - 1) / kThreads;
+  if (grid > INT32_MAX) return pkv__fail(PKV_EINVAL, "write too large");
+  hipLaunchKernelGGL(kv_write_kernel, dim3((uint32_t)grid), dim3(kThreads), 0,
+                     (hipStream_t)stream, (const uint4*)k, (const uint4*)v, slot_mapping,
+                     (uint4*)k_cache, (uint4*)v_cache, c->num_kv_heads, c->block_size,
+                     row_chunks, total, (int64_t)c->num_blocks * c->block_size);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return pkv__fail(PKV_EHIP, "kv_write launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+extern "C" int pkv_copy_blocks(void* k_cache, void* v_cache, const pkv_cache_desc* c,
+                               const int32_t* src_dst_pairs, int32_t num_pairs, void* stream) {
+  pkv__clear_error();
+  int rc = pkv__check_desc(c);
+  if (rc) return rc;
+  if (num_pairs < 0) return pkv__fail(PKV_EINVAL, "num_pairs %d < 0", num_pairs);
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !src_dst_pairs) return pkv__fail(PKV_EINVAL, "NULL device pointer");
+  if (!aligned16(k_cache) || !aligned16(v_cache) || ((uintptr_t)src_dst_pairs & 7u))
+    return pkv__fail(PKV_EINVAL, "caches must be 16-byte aligned, pairs 8-byte aligned");
+  const int64_t block_bytes =
+      (int64_t)c->num_kv_heads * c->block_size * c->head_dim * elem_bytes(c->dtype);
+  if (block_bytes % 16 != 0 || block_bytes / 16 > INT32_MAX)
+    return pkv__fail(PKV_EUNSUPPORTED, "block of %lld bytes is not a multiple of 16",
+                     (long long)block_bytes);
+  const int32_t block_chunks = (int32_t)(block_bytes / 16);
+  const int32_t per_group = kThreads * kPerThread;
+  const int32_t groups = (block_chunks + per_group - 1) / per_group;
+  const int64_t grid = (int64_t)num_pairs * groups;
+  if (grid > INT32_MAX) return pkv__fail(PKV_EINVAL, "copy too large");
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((uint32_t)grid), dim3(kThreads), 0,
+                     (hipStream_t)stream, (uint4*)k_cache, (uint4*)v_cache, src_dst_pairs,
+                     block_chunks, groups, c->num_blocks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return pkv__fail(PKV_EHIP, "copy_blocks launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}

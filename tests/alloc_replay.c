@@ -1,0 +1,94 @@
+/* Replays an allocator op stream read from stdin and prints every result, so
+ * the allocator can run under AddressSanitizer / UBSan in a plain gcc build.
+ * Input lines:  N B perm...  then  add s n | fork p c | append s |
+ *               step k s1..sk | free s | table s
+ * Output: one line per op with the return code and results. */
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "pagedkv.h"
+
+int main(void) {
+  int n, b;
+  if (scanf("%d %d", &n, &b) != 2) return 2;
+  int* perm = malloc(sizeof(int) * n);
+  for (int i = 0; i < n; ++i)
+    if (scanf("%d", &perm[i]) != 1) return 2;
+  pkv_alloc* a = pkv_alloc_create(n, b, perm);
+  free(perm);
+  if (!a) return 3;
+  char op[16];
+  while (scanf("%15s", op) == 1) {
+    if (op[0] == 'a' && op[1] == 'd') {
+      long long s; int k;
+      if (scanf("%lld %d", &s, &k) != 2) return 2;
+      int64_t* slots = malloc(sizeof(int64_t) * (k > 0 ? k : 1));
+      int rc = pkv_seq_add(a, s, k, slots);
+      printf("add %d", rc);
+      if (rc == 0) for (int i = 0; i < k; ++i) printf(" %lld", (long long)slots[i]);
+      printf("\n");
+      free(slots);
+    } else if (op[0] == 'f' && op[1] == 'o') {
+      long long p, c;
+      if (scanf("%lld %lld", &p, &c) != 2) return 2;
+      printf("fork %d\n", pkv_seq_fork(a, p, c));
+    } else if (op[0] == 'a') {
+      long long s; int64_t slot; int32_t cow[2];
+      if (scanf("%lld", &s) != 1) return 2;
+      int rc = pkv_seq_append(a, s, &slot, cow);
+      if (rc == 0) printf("append 0 %lld %d %d\n", (long long)slot, cow[0], cow[1]);
+      else printf("append %d\n", rc);
+    } else if (op[0] == 's') {
+      int k;
+      if (scanf("%d", &k) != 1) return 2;
+      int64_t* ids = malloc(sizeof(int64_t) * (k > 0 ? k : 1));
+      int64_t* slots = malloc(sizeof(int64_t) * (k > 0 ? k : 1));
+      int32_t* pairs = malloc(sizeof(int32_t) * 2 * (k > 0 ? k : 1));
+      for (int i = 0; i < k; ++i) { long long x; if (scanf("%lld", &x) != 1) return 2; ids[i] = x; }
+      int32_t nc = 0;
+      int rc = pkv_step_append(a, ids, k, slots, pairs, &nc);
+      printf("step %d", rc);
+      if (rc == 0) {
+        for (int i = 0; i < k; ++i) printf(" %lld", (long long)slots[i]);
+        printf(" |");
+        for (int i = 0; i < nc; ++i) printf(" %d %d", pairs[2 * i], pairs[2 * i + 1]);
+      }
+      printf("\n");
+      free(ids); free(slots); free(pairs);
+    } else if (op[0] == 'f') {
+      long long s;
+      if (scanf("%lld", &s) != 1) return 2;
+      printf("free %d\n", pkv_seq_free(a, s));
+    } else if (op[0] == 't') {
+      long long s; int32_t len, nb;
+      if (scanf("%lld", &s) != 1) return 2;
+      int rc = pkv_seq_info(a, s, &len, &nb);
+      printf("table %d", rc);
+      if (rc == 0) {
+        int32_t* row = malloc(sizeof(int32_t) * (nb > 0 ? nb : 1));
+        int64_t id = s; int32_t l2;
+        pkv_build_tables(a, &id, 1, row, nb, &l2);
+        printf(" %d :", len);
+        for (int i = 0; i < nb; ++i) printf(" %d", row[i]);
+        free(row);
+      }
+      printf("\n");
+    } else {
+      return 2;
+    }
+  }
+  int32_t* fifo = malloc(sizeof(int32_t) * n);
+  int32_t* ref = malloc(sizeof(int32_t) * n);
+  int32_t nf;
+  pkv_alloc_export(a, fifo, &nf, ref);
+  printf("final free");
+  for (int i = 0; i < nf; ++i) printf(" %d", fifo[i]);
+  printf(" | ref");
+  for (int i = 0; i < n; ++i) printf(" %d", ref[i]);
+  printf("\n");
+  pkv_stats st;
+  pkv_alloc_stats(a, &st);
+  free(fifo); free(ref);
+  pkv_alloc_destroy(a);
+  return 0;
+}
