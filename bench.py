@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--replicas", type=int, default=1,
                     help="rotate over R copies of the KV pool (step i uses copy i %% R)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="instead of the benchmark, time a plain device copy of this many MiB "
+                         "(the reference kernel for HBM counter calibration and the copy ceiling)")
     return ap.parse_args()
 
 
@@ -159,6 +162,30 @@ def cpu_baseline(wl: Workload, budget_s: float = 20.0):
             "seqs_per_s": len(seqs) / dt}
 
 
+def copy_probe(mib: int, reps: int) -> None:
+    """Plain device-to-device copy of a known size: reads and writes mib MiB."""
+    import torch
+
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(7)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)[reps // 2]
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n,
+                      "median_ms": round(ms, 4), "gbps_read_plus_write": round(2 * n / ms / 1e6, 1)}),
+          flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -171,6 +198,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib, max(args.steps, 1))
+        return
     total = args.warmup + args.steps
     t_setup = time.perf_counter()
     wl = Workload(args.workload, args.block_size, total)
