@@ -130,6 +130,30 @@ class Workload:
         return self.kv_bytes(i) + qo + 4 * blocks * sh.num_kv_heads + 4 * sh.num_seqs
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+DECODE_SOURCE = os.path.join(ROOT, "paged_kv_cache_377_amd", "csrc", "decode.hip")
+
+
+def measured_traffic(workload: int, block_size, partition_size: int):
+    """HBM bytes per decode call from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    runs (scaled by the copy calibration), or None when there is no such run
+    for this configuration or the decode source has changed since it was taken."""
+    import hashlib
+
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        with open(DECODE_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if (rec.get("decode_source_sha256") != sha or rec.get("workload") != workload
+            or rec.get("block_size") != (block_size or 16)
+            or rec.get("partition_size") != partition_size):
+        return None
+    return int(rec["hbm_bytes_per_call"])
+
+
 def to_dev(a, torch):
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint16:
@@ -225,40 +249,52 @@ def main():
                                               args.partition_size) for d in dsteps)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(total)]
     torch.cuda.synchronize()
 
     def step(i):
         d = dsteps[i]
         kc, vc = kcs[i % R], vcs[i % R]
-        ev[i][0].record(stream)
         if d["pairs"] is not None:
             pkv.copy_blocks(kc, vc, d["pairs"], stream=stream)
         pkv.paged_kv_write(d["k"], d["v"], d["slots"], kc, vc, stream=stream)
-        ev[i][1].record(stream)
-        pkv.paged_attention_decode(out, d["q"], kc, vc, d["tables"], d["ctx"], sh.scale,
-                                   d["max_ctx"], args.partition_size, workspace=workspace,
-                                   stream=stream)
-        ev[i][2].record(stream)
+        decode(i)
+
+    def decode(i):
+        d = dsteps[i]
+        pkv.paged_attention_decode(out, d["q"], kcs[i % R], vcs[i % R], d["tables"], d["ctx"],
+                                   sh.scale, d["max_ctx"], args.partition_size,
+                                   workspace=workspace, stream=stream)
 
     for i in range(args.warmup):
         step(i)
+    # Timed region: K whole steps, no events or syncs inside.
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.warmup, total):
         step(i)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    step_gpu_ms = ev0.elapsed_time(ev1) / args.steps
+
+    # Decode launch duration: the same K decode calls again, back to back on
+    # the stream (every token they read is already written), between two events.
+    ev2, ev3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev2.record(stream)
+    for i in range(args.warmup, total):
+        decode(i)
+    ev3.record(stream)
+    torch.cuda.synchronize()
+    dec_avg_ms = ev2.elapsed_time(ev3) / args.steps
 
     timed = range(args.warmup, total)
-    step_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in timed]
-    dec_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in timed]
     kv = sum(wl.kv_bytes(i) for i in timed)
     alg = sum(wl.algorithmic_bytes(i) for i in timed)
     ms_per_step = wall * 1e3 / args.steps
     value = kv / (wall) / 1e9
-    dec_avg_ms = sum(dec_ms) / len(dec_ms)
     achieved = alg / args.steps / (dec_avg_ms * 1e-3) / 1e9
     res = {
         "metric": "paged-decode KV-read GB/s",
@@ -280,12 +316,15 @@ def main():
                    "mean_context": float(np.mean([wl.steps[i]["ctx"].mean() for i in timed])),
                    "replicas": R},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
-        "decode_seqs_per_s": round(sh.num_seqs / (ms_per_step * 1e-3), 1),
-        "event_ms_per_step": round(sum(step_ms) / len(step_ms), 4),
+        "decode_seqs_per_s": round(sh.num_seqs / (dec_avg_ms * 1e-3), 1),
+        "step_seqs_per_s": round(sh.num_seqs / (ms_per_step * 1e-3), 1),
+        "event_ms_per_step": round(step_gpu_ms, 4),
         "decode_ms": round(dec_avg_ms, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "paged_attention_decode (partition + reduce)",
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(args.workload, args.block_size,
+                                                 args.partition_size),
+                     "kernel": "paged_attention_decode (partition + reduce launches)",
                      "algorithmic_bytes_per_launch": int(alg / args.steps)},
         "allocator_us_per_step": None,
     }

@@ -33,6 +33,9 @@ HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
     # packed FP32 VALU ops stay off; hipcc -O3 would otherwise form them
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in ordinary VGPRs: the decode rescales them with
+    # VALU ops, which would otherwise copy them out of and back into AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     "-I", INCLUDE, "-I", CSRC,
 ]

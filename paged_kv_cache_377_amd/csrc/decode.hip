@@ -7,27 +7,39 @@
 // the block table.  The table lives in GPU memory and is read inside the
 // kernel (weishuz.com Month 2, section 02, row "TLB").
 //
-// Work decomposition.  One workgroup (4 waves of 64 lanes) per (sequence,
-// KV head, partition of `ps` tokens).  The query heads sharing the KV head
-// (the group of G = Hq / Hkv heads) are processed together, so each K/V byte
-// is read from HBM once per step.  Wave w walks blocks w, w+4, ... of its
-// partition with an online softmax; the four waves merge through LDS.  A
-// sequence that fits one partition writes its output directly; otherwise
-// each partition writes (max, sum, unnormalised output) and a small reduce
-// kernel combines them.
+// Work decomposition (both kernels).  One workgroup (4 waves of 64 lanes) per
+// (sequence, KV head, partition of `ps` tokens).  The query heads sharing the
+// KV head (the group of G = Hq / Hkv heads) are processed together, so each
+// K/V byte is read from HBM once per step.  Each wave keeps an online softmax
+// over its share of the partition; the four waves merge through LDS.  A
+// sequence that fits one partition writes its output directly; otherwise each
+// partition writes (max, sum, unnormalised output) and a small reduce kernel
+// combines them.
 //
-// Lane layout.  A (block, head) run is block_size rows of head_dim elements.
-// Each lane loads 16 bytes (EPL elements) of a row; LPT = head_dim / EPL
-// lanes cover one token row and one wave load covers TPL = 64 / LPT tokens
-// (1 KiB, contiguous).  Dot products are summed over the LPT lanes of a
-// token with DPP row operations; the token's softmax weight is then already
-// in every lane that holds a piece of its V row, and the P*V products
-// accumulate per lane with no exchange until the end of the partition.
+// bf16 caches: decode_partition_mfma_kernel.  The per-token work is two small
+// dense contractions (scores = K q^T, output = P V), run on the matrix cores
+// (v_mfma_f32_16x16x32_bf16) over tiles of 16 tokens:
+//   * scores: A = 16 K rows (tokens), B = the group's query rows (columns =
+//     heads, zero-padded to 16);
+//   * V^T: V is stored token-major, but the output product contracts over
+//     tokens, so each 16x16 tile of V is transposed by multiplying the 16 V
+//     rows with a 0/1 selection matrix (exact: one non-zero term per output);
+//   * output: A = V^T tile (rows = 16 dims), B = P (columns = heads), with P
+//     split into a bf16 high part and a bf16 low part (both in the contraction)
+//     so the weights keep ~16 significant bits.
+// The output tile of a head lands in the lanes that hold that head's softmax
+// statistics, so rescaling needs no data exchange.  The running maximum is
+// only moved when a tile's maximum exceeds it by more than 2^8 (log2 units),
+// which keeps every weight <= 2^8 and makes rescales rare.
 //
-// Numerics: fp32 throughout, logits in the base-2 domain (q is pre-scaled by
-// scale * log2 e, exponentials are exp2), output rounded to the cache dtype
-// (bf16: round-to-nearest-even).  Masked tokens are selected out, never
-// multiplied by zero, so NaN bits in unfilled slots cannot reach the result.
+// fp32 caches: decode_partition_valu_kernel.  Each lane loads 16 bytes of a
+// K/V row; dot products are summed over the lanes of a row with DPP row
+// operations and P*V accumulates per lane in fp32 FMAs.
+//
+// Numerics: fp32 accumulation, logits in the base-2 domain (scale * log2 e),
+// exponentials are exp2, output rounded to the cache dtype (bf16:
+// round-to-nearest-even).  Masked tokens are selected out, never multiplied
+// by zero, so NaN bits in unfilled slots cannot reach the result.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -125,16 +137,52 @@ __device__ inline float across_max(float x) {
 // ------------------------------------------------------------ partition
 
 // Workspace layout for P > 1:
-//   part_ml [S][Hq][P][2] f32  (running max in log2 units, sum of weights)
+//   part_ml [S][Hq][P][2] f32  (reference max in log2 units, sum of weights)
 //   part_o  [S][Hq][P][D] f32  (unnormalised weighted sum of V)
+//
+// Combine the four waves' (m, l, o) of one workgroup, held in LDS, and write
+// either the final output row (the sequence has one partition) or this
+// partition's partial.  Must be called by all kThreads threads after a barrier.
+template <typename T, int D, int G>
+__device__ inline void merge_waves(const float (&sm_m)[kWaves][G], const float (&sm_l)[kWaves][G],
+                                   const float (&sm_o)[kWaves][G][D], int64_t row0, int p,
+                                   int num_parts, int nparts_s, T* __restrict__ out,
+                                   float* __restrict__ part_ml, float* __restrict__ part_o) {
+  for (int i = threadIdx.x; i < G * D; i += kThreads) {
+    const int h = i / D;
+    const int d = i - h * D;
+    float mx = sm_m[0][h];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, sm_m[w][h]);
+    float L = 0.0f, O = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      // a wave that saw no token has m = -inf and contributes nothing
+      const float f = sm_m[w][h] == -INFINITY ? 0.0f : exp2f(sm_m[w][h] - mx);
+      L = fmaf(sm_l[w][h], f, L);
+      O = fmaf(sm_o[w][h][d], f, O);
+    }
+    const int64_t row = row0 + h;
+    if (nparts_s == 1) {
+      store_out(out + row * D + d, O / L);
+    } else {
+      part_o[(row * num_parts + p) * D + d] = O;
+      if (d == 0) {
+        part_ml[(row * num_parts + p) * 2 + 0] = mx;
+        part_ml[(row * num_parts + p) * 2 + 1] = L;
+      }
+    }
+  }
+}
+
 template <typename E, int D, int B, int G>
-__global__ __launch_bounds__(kThreads) void decode_partition_kernel(
+__global__ __launch_bounds__(kThreads) void decode_partition_valu_kernel(
     const typename E::raw* __restrict__ q, const uint4* __restrict__ k_cache,
     const uint4* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     int32_t table_width, const int32_t* __restrict__ context_lens,
     typename E::raw* __restrict__ out, float* __restrict__ part_ml,
-    float* __restrict__ part_o, int32_t num_kv_heads, int32_t num_blocks, int32_t num_parts,
-    int32_t ps, int32_t max_context_len, float qscale) {
+    float* __restrict__ part_o, int32_t num_seqs, int32_t num_kv_heads, int32_t num_blocks,
+    int32_t num_parts, int32_t ps, int32_t max_context_len, float qscale) {
   constexpr int EPL = 16 / E::bytes;  // elements per lane load
   constexpr int LPT = D / EPL;        // lanes per token row
   constexpr int TPL = kWave / LPT;    // tokens per wave load
@@ -143,10 +191,15 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int p = blockIdx.x % num_parts;
-  const int sg = blockIdx.x / num_parts;
-  const int g = sg % num_kv_heads;
-  const int s = sg / num_kv_heads;
+  // Grid order (partition, sequence, KV head), KV head fastest: workgroups
+  // are dealt round-robin to the XCDs, so consecutive ids must carry similar
+  // work.  With the partition fastest, every sequence's partition 0 (always
+  // present) would land on one XCD and its late, mostly empty partitions on
+  // another.
+  const int g = blockIdx.x % num_kv_heads;
+  const int ps_idx = blockIdx.x / num_kv_heads;
+  const int s = ps_idx % num_seqs;
+  const int p = ps_idx / num_seqs;
   const int hq = num_kv_heads * G;
   // Lengths outside [0, max_context_len] break the caller's contract; clamping
   // keeps every table, cache and workspace access in bounds regardless.
@@ -289,31 +342,239 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(
   }
   __syncthreads();
 
-  for (int i = threadIdx.x; i < G * D; i += kThreads) {
-    const int h = i / D;
-    const int d = i - h * D;
-    float mx = sm_m[0][h];
+  merge_waves<typename E::raw, D, G>(sm_m, sm_l, sm_o, (int64_t)s * hq + g * G, p, num_parts,
+                                    nparts_s, out, part_ml, part_o);
+}
+
+// ------------------------------------------------------------ MFMA (bf16)
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// D = A B + C on a 16x16x32 bf16 tile.  Lane l supplies row (l % 16) of A and
+// column (l % 16) of B, each as 8 consecutive k-slots of group l / 16; it
+// receives D[4 (l / 16) + r][l % 16] in element r.  Only the pairing of A's
+// and B's k-slots matters to the kernel, not their order.
+__device__ inline f32x4_t mfma16x16x32(const uint4& a, const uint4& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Two fp32 values that are exactly bf16 numbers -> one packed bf16 pair.
+__device__ inline uint32_t pack_bf16_pair(float lo, float hi) {
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// A tile's maximum must exceed the reference maximum by more than this (log2
+// units) before the accumulators are rescaled; weights stay <= 2^8.
+constexpr float kRescaleSlack = 8.0f;
+
+template <int D, int B, int G>
+__global__ __launch_bounds__(kThreads) void decode_partition_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
+    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
+    int32_t table_width, const int32_t* __restrict__ context_lens, uint16_t* __restrict__ out,
+    float* __restrict__ part_ml, float* __restrict__ part_o, int32_t num_seqs,
+    int32_t num_kv_heads, int32_t num_blocks, int32_t num_parts, int32_t ps,
+    int32_t max_context_len, float qscale) {
+  constexpr int KP = D / 32;           // 32-dim pieces of a row: one 16-byte load per lane each
+  constexpr int DT = D / 16;           // 16-dim output tiles
+  constexpr int kTile = 16;            // tokens per MFMA tile
+  constexpr int kChunkTiles = 64;      // tiles whose table entries are staged at once
+  constexpr int kChunkEntries = kChunkTiles * kTile / B + 2;
+  static_assert(D % 32 == 0 && G >= 1 && G <= 16, "unsupported shape");
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int col = lane & 15;  // token row of the loads; head column of scores and outputs
+  const int grp = lane >> 4;  // k-slot group of the operands; row group of the results
+  // Grid order (partition, sequence, KV head), KV head fastest: workgroups
+  // are dealt round-robin to the XCDs, so consecutive ids must carry similar
+  // work.  With the partition fastest, every sequence's partition 0 (always
+  // present) would land on one XCD and its late, mostly empty partitions on
+  // another.
+  const int g = blockIdx.x % num_kv_heads;
+  const int ps_idx = blockIdx.x / num_kv_heads;
+  const int s = ps_idx % num_seqs;
+  const int p = ps_idx / num_seqs;
+  const int hq = num_kv_heads * G;
+  // Lengths outside [0, max_context_len] break the caller's contract; clamping
+  // keeps every table, cache and workspace access in bounds regardless.
+  const int n = min(max(context_lens[s], 0), max_context_len);
+  const int t0 = p * ps;
+
+  if (n == 0) {
+    if (p != 0) return;
+    for (int i = threadIdx.x; i < G * D; i += kThreads)
+      store_out(out + ((int64_t)s * hq + g * G) * D + i, 0.0f);
+    return;
+  }
+  if (t0 >= n) return;  // partition past the end of this sequence
+  const int t1 = min(n, t0 + ps);
+  const int ntiles = (t1 - t0 + kTile - 1) / kTile;
+  const int nparts_s = (n + ps - 1) / ps;
+
+  // k-slot (grp, e) of piece kk is dim 32 kk + 8 grp + e, for K rows and q alike.
+  uint4 qb[KP];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, sm_m[w][h]);
-    float L = 0.0f, O = 0.0f;
+  for (int kk = 0; kk < KP; ++kk)
+    qb[kk] = col < G ? *reinterpret_cast<const uint4*>(q + ((int64_t)s * hq + g * G + col) * D +
+                                                       32 * kk + 8 * grp)
+                     : make_uint4(0, 0, 0, 0);
+
+  // Selection matrices: column c of half h picks dim 16 h + c of a 32-dim
+  // piece, i.e. k-slot (2 h + c / 8, c % 8).  bf16 1.0 = 0x3f80.
+  uint4 sel[2];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      // a wave that saw no block has m = -inf and contributes nothing
-      const float f = sm_m[w][h] == -INFINITY ? 0.0f : exp2f(sm_m[w][h] - mx);
-      L = fmaf(sm_l[w][h], f, L);
-      O = fmaf(sm_o[w][h][d], f, O);
+  for (int h = 0; h < 2; ++h) {
+    const bool on = grp == 2 * h + (col >> 3);
+    const int e = col & 7;
+    const uint32_t one = 0x3f80u << (16 * (e & 1));
+    sel[h] = make_uint4(on && (e >> 1) == 0 ? one : 0u, on && (e >> 1) == 1 ? one : 0u,
+                        on && (e >> 1) == 2 ? one : 0u, on && (e >> 1) == 3 ? one : 0u);
+  }
+
+  f32x4_t o[DT];
+#pragma unroll
+  for (int j = 0; j < DT; ++j) o[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float m = -INFINITY;  // reference maximum of head `col` (log2 units)
+  float l = 0.0f;       // this lane's share of the weight sum of head `col`
+
+  __shared__ int32_t sm_bt[kChunkEntries];
+  __shared__ float sm_m[kWaves][G];
+  __shared__ float sm_l[kWaves][G];
+  __shared__ float sm_o[kWaves][G][D];
+
+  const int32_t* bt = block_tables + (int64_t)s * table_width;
+  const int64_t blk_stride = (int64_t)num_kv_heads * B * D;
+  const int64_t head_off = (int64_t)g * B * D + 8 * grp;
+
+  // The K and V pieces of token row `col` of a tile.  The loads are not
+  // predicated, so the compiler can keep the next tile's loads in flight
+  // while the current tile is processed: a row past the partition (or whose
+  // block id is outside the pool) reads this lane's query piece instead, a
+  // small in-bounds row, and its V is replaced by zeros when it is used.
+  const uint16_t* q_safe = q + ((int64_t)s * hq + g * G) * D + 8 * grp;
+  struct Tile {
+    uint4 k[KP], v[KP];
+    bool ok;
+  };
+  auto load_tile = [&](int tile, int cb0, Tile& x) {
+    const int t = t0 + tile * kTile + col;
+    const bool live = tile >= 0 && t < t1;
+    const int tc = live ? t : t1 - 1;  // stays inside the staged chunk
+    const int phys = sm_bt[tc / B - cb0];
+    x.ok = live && phys >= 0 && phys < num_blocks;
+    const int64_t off = (int64_t)phys * blk_stride + head_off + (int64_t)(tc % B) * D;
+    const uint16_t* kp = x.ok ? k_cache + off : q_safe;
+    const uint16_t* vp = x.ok ? v_cache + off : q_safe;
+#pragma unroll
+    for (int kk = 0; kk < KP; ++kk) {
+      x.k[kk] = *reinterpret_cast<const uint4*>(kp + 32 * kk);
+      x.v[kk] = *reinterpret_cast<const uint4*>(vp + 32 * kk);
     }
-    const int64_t row = (int64_t)s * hq + g * G + h;
-    if (nparts_s == 1) {
-      store_out(out + row * D + d, O / L);
-    } else {
-      part_o[(row * num_parts + p) * D + d] = O;
-      if (d == 0) {
-        part_ml[(row * num_parts + p) * 2 + 0] = mx;
-        part_ml[(row * num_parts + p) * 2 + 1] = L;
-      }
+  };
+
+  auto process = [&](int tile, Tile& x) {
+    // scores of tokens 4 grp + r (tile rows) for head `col`; rows that are
+    // not live are replaced by -inf below, whatever their K bits were
+    f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < KP; ++kk) sc = mfma16x16x32(x.k[kk], qb[kk], sc);
+    // V rows that are not live become zeros (their weight is 0, and 0 * NaN
+    // would otherwise poison the output)
+#pragma unroll
+    for (int kk = 0; kk < KP; ++kk)
+      if (!x.ok) x.v[kk] = make_uint4(0, 0, 0, 0);
+    const int tb = t0 + tile * kTile + 4 * grp;
+    float sv[4];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sv[r] = tb + r < t1 ? sc[r] * qscale : -INFINITY;
+      bm = fmaxf(bm, sv[r]);
+    }
+    bm = fmaxf(bm, xor16(bm));
+    bm = fmaxf(bm, xor32(bm));  // maximum over the tile's 16 tokens
+    const bool need = bm > m + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float alpha = need ? fast_exp2(m - bm) : 1.0f;  // 0 on the first tile
+      m = need ? bm : m;
+      l *= alpha;
+#pragma unroll
+      for (int j = 0; j < DT; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[j][r] *= alpha;
+    }
+    float pw[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pw[r] = fast_exp2(sv[r] - m);  // masked rows: exactly 0
+    l += (pw[0] + pw[1]) + (pw[2] + pw[3]);
+    // P as the B operand: k-slots e < 4 hold the bf16 high parts of the
+    // weights of tokens 4 grp + e, slots e >= 4 the rounded remainders.
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      hi[r] = __float_as_uint(pw[r]) & 0xffff0000u;
+      lo[r] = (__float_as_uint(pw[r] - __uint_as_float(hi[r])) + 0x8000u) & 0xffff0000u;
+    }
+    const uint4 pb = make_uint4((hi[0] >> 16) | hi[1], (hi[2] >> 16) | hi[3],
+                                (lo[0] >> 16) | lo[1], (lo[2] >> 16) | lo[3]);
+#pragma unroll
+    for (int j = 0; j < DT; ++j) {
+      // V^T tile j: element r = V[token 4 grp + r][dim 16 j + col], exact
+      const f32x4_t tv = mfma16x16x32(x.v[j >> 1], sel[j & 1], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
+      const uint32_t a01 = pack_bf16_pair(tv[0], tv[1]);
+      const uint32_t a23 = pack_bf16_pair(tv[2], tv[3]);
+      // o[j] element r += sum_t V[t][dim 16 j + 4 grp + r] * P[t][head col]
+      o[j] = mfma16x16x32(make_uint4(a01, a23, a01, a23), pb, o[j]);
+    }
+  };
+
+  for (int c0 = 0; c0 < ntiles; c0 += kChunkTiles) {
+    const int c1 = min(ntiles, c0 + kChunkTiles);
+    const int cb0 = (t0 + c0 * kTile) / B;
+    const int cb1 = (min(t1, t0 + c1 * kTile) - 1) / B + 1;
+    __syncthreads();  // the previous chunk's entries are no longer read
+    for (int i = threadIdx.x; i < cb1 - cb0; i += kThreads) sm_bt[i] = bt[cb0 + i];
+    __syncthreads();
+    int tile = c0 + wave;
+    if (tile >= c1) continue;
+    // Two tile buffers in turn: the loads of the tile after the current one
+    // (or of a dummy row past the chunk's end) are issued before the current
+    // tile is processed.
+    Tile ta, tb;
+    load_tile(tile, cb0, ta);
+    for (;;) {
+      load_tile(tile + kWaves < c1 ? tile + kWaves : -1, cb0, tb);
+      process(tile, ta);
+      tile += kWaves;
+      if (tile >= c1) break;
+      load_tile(tile + kWaves < c1 ? tile + kWaves : -1, cb0, ta);
+      process(tile, tb);
+      tile += kWaves;
+      if (tile >= c1) break;
     }
   }
+
+  // the four row groups of a head hold disjoint tokens' weight sums
+  l += xor16(l);
+  l += xor32(l);
+  if (grp == 0 && col < G) {
+    sm_m[wave][col] = m;
+    sm_l[wave][col] = l;
+  }
+  if (col < G) {
+#pragma unroll
+    for (int j = 0; j < DT; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm_o[wave][col][16 * j + 4 * grp + r] = o[j][r];
+  }
+  __syncthreads();
+  merge_waves<uint16_t, D, G>(sm_m, sm_l, sm_o, (int64_t)s * hq + g * G, p, num_parts, nparts_s,
+                              out, part_ml, part_o);
 }
 
 // --------------------------------------------------------------- reduce
@@ -371,12 +632,21 @@ template <typename E, int D, int B, int G>
 int launch(const LaunchArgs& a) {
   const int64_t grid = (int64_t)a.num_seqs * a.num_kv_heads * a.num_parts;
   if (grid > INT32_MAX) return pkv__fail(PKV_EINVAL, "decode grid too large");
-  hipLaunchKernelGGL((decode_partition_kernel<E, D, B, G>), dim3((uint32_t)grid),
-                     dim3(kThreads), 0, a.stream, (const typename E::raw*)a.q,
-                     (const uint4*)a.k_cache, (const uint4*)a.v_cache, a.block_tables,
-                     a.width, a.context_lens, (typename E::raw*)a.out, a.part_ml, a.part_o,
-                     a.num_kv_heads, a.num_blocks, a.num_parts, a.ps, a.max_context_len,
-                     a.qscale);
+  if constexpr (E::bytes == 2) {
+    hipLaunchKernelGGL((decode_partition_mfma_kernel<D, B, G>), dim3((uint32_t)grid),
+                       dim3(kThreads), 0, a.stream, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.block_tables,
+                       a.width, a.context_lens, (uint16_t*)a.out, a.part_ml, a.part_o,
+                       a.num_seqs, a.num_kv_heads, a.num_blocks, a.num_parts, a.ps, a.max_context_len,
+                       a.qscale);
+  } else {
+    hipLaunchKernelGGL((decode_partition_valu_kernel<E, D, B, G>), dim3((uint32_t)grid),
+                       dim3(kThreads), 0, a.stream, (const typename E::raw*)a.q,
+                       (const uint4*)a.k_cache, (const uint4*)a.v_cache, a.block_tables,
+                       a.width, a.context_lens, (typename E::raw*)a.out, a.part_ml, a.part_o,
+                       a.num_seqs, a.num_kv_heads, a.num_blocks, a.num_parts, a.ps, a.max_context_len,
+                       a.qscale);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return pkv__fail(PKV_EHIP, "decode_partition launch: %s", hipGetErrorString(e));
   if (a.num_parts > 1) {
