@@ -52,7 +52,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2, choices=[2, 4, 5])
     ap.add_argument("--block-size", type=int, default=None)
-    ap.add_argument("--partition-size", type=int, default=512)
+    ap.add_argument("--partition-size", type=int, default=-1,
+                    help="-1: balanced split (default); > 0: split-context partitions; 0: no split")
     ap.add_argument("--replicas", type=int, default=1,
                     help="rotate over R copies of the KV pool (step i uses copy i %% R)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -245,7 +246,8 @@ def main():
             pairs=to_dev(st["pairs"], torch) if len(st["pairs"]) else None,
             max_ctx=int(st["ctx"].max())))
     out = torch.empty_like(dsteps[0]["q"])
-    ws_bytes = max(pkv.decode_workspace_bytes(sh.num_seqs, sh.num_q_heads, sh.head_dim, d["max_ctx"],
+    desc = pkv.cache_desc(kcs[0])
+    ws_bytes = max(pkv.decode_workspace_bytes(desc, sh.num_seqs, sh.num_q_heads, d["max_ctx"],
                                               args.partition_size) for d in dsteps)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()

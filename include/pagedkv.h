@@ -96,16 +96,23 @@ int pkv_paged_kv_write(const void* k, const void* v, const int64_t* slot_mapping
 int pkv_copy_blocks(void* k_cache, void* v_cache, const pkv_cache_desc* c,
                     const int32_t* src_dst_pairs, int32_t num_pairs, void* stream);
 
+/* partition_size value: let the library split the work (see below). */
+enum { PKV_PARTITION_AUTO = -1 };
+
 /*
  * Bytes of device workspace pkv_paged_attention_decode needs for these sizes
- * (0 when every sequence fits one partition).  partition_size as below.
+ * and this partition_size, on the current HIP device (0 when the call needs
+ * none, and 0 with pkv_last_error() set on invalid arguments).  With
+ * PKV_PARTITION_AUTO the figure depends on the device's compute-unit count,
+ * so size the workspace on the device that runs the decode.
  */
-size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                  int32_t max_context_len, int32_t partition_size);
+size_t pkv_decode_workspace_bytes(const pkv_cache_desc* c, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t max_context_len,
+                                  int32_t partition_size);
 
 /*
  * Decode attention: one query token per sequence against that sequence's
- * cached K/V, read through its block table (blog section 3(3), step 2):
+ * cached K/V, read through its block table (blog section 3(3), step 2:
  * attention is computed over the logically contiguous tokens while the data
  * comes from physical blocks; weishuz.com Month 2, section 06: the kernel is
  * ordinary attention whose only difference is gathering K and V from
@@ -121,20 +128,33 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *
  *   out           device, [num_seqs, num_q_heads, head_dim], dtype
  *   q             device, [num_seqs, num_q_heads, head_dim], dtype
- *   block_tables  device, [num_seqs, max_blocks_per_seq] int32; only the
- *                 first ceil(context_lens[s] / block_size) entries of row s
- *                 are read and each must be in [0, num_blocks)
+ *   block_tables  device, [num_seqs, max_blocks_per_seq] int32; the first
+ *                 ceil(context_lens[s] / block_size) entries of row s are used
+ *                 and each must be in [0, num_blocks) (an entry outside the
+ *                 pool is never dereferenced; the result is then unspecified);
+ *                 later entries of the row may be read but are never used
  *   context_lens  device, [num_seqs] int32, each in [0, max_context_len]; it
  *                 counts the token just written by pkv_paged_kv_write
  *   max_context_len  host int, bound on context_lens (sizes the launch)
- *   partition_size   tokens per split-context partition: a multiple of
- *                 block_size and of 64, or 0 for no split (one partition
- *                 holds the whole context)
+ *   partition_size   how the work is split:
+ *                 PKV_PARTITION_AUTO: bf16 caches with num_seqs <= 8191 use a
+ *                   balanced split: every worker wave of the GPU reads an
+ *                   equal share of all sequences' 16-token tiles (ragged
+ *                   context lengths cannot unbalance it), and the sequences
+ *                   whose tiles several workers share are combined by a second
+ *                   kernel; otherwise as partition_size 512;
+ *                 a positive multiple of block_size: split-context partitions
+ *                   of that many tokens, one workgroup each, then a combine
+ *                   kernel when a sequence spans several;
+ *                 0: no split (one workgroup per sequence and KV head).
  *   workspace     device, >= pkv_decode_workspace_bytes(...) bytes (may be
- *                 NULL when that is 0); contents need no initialisation
- * Slots at positions >= n and blocks the table does not reach are never read
- * (any bits, NaN included, leave the result unchanged).  The result does not
- * depend on physical block ids and is the same on every run (no atomics).
+ *                 NULL when that is 0), 16-byte aligned; contents need no
+ *                 initialisation and are scratch between calls
+ * Slots at positions >= n and blocks the table does not reach are never
+ * used (any bits, NaN included, leave the result unchanged).  The result does
+ * not depend on physical block ids and is the same on every run (no atomics;
+ * every combine runs in a fixed order).  Calls that share one workspace must
+ * be ordered (one stream).
  * Errors: PKV_EINVAL (null pointer, bad sizes, workspace too small, partition
  * size not allowed), PKV_EUNSUPPORTED, PKV_EHIP.
  */

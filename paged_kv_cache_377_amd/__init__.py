@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     PKV_ERANGE,
     PKV_EUNSUPPORTED,
     PKV_F32,
+    PKV_PARTITION_AUTO,
     PKV_OK,
     BlockAllocator,
     CacheDesc,

@@ -22,6 +22,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "pagedkv.h")
 
 PKV_OK, PKV_EINVAL, PKV_ENOBLOCKS, PKV_ERANGE, PKV_EHIP, PKV_EUNSUPPORTED = 0, -1, -2, -3, -4, -5
 PKV_F32, PKV_BF16 = 0, 1
+PKV_PARTITION_AUTO = -1
 _NAMES = {0: "PKV_OK", -1: "PKV_EINVAL", -2: "PKV_ENOBLOCKS", -3: "PKV_ERANGE", -4: "PKV_EHIP",
           -5: "PKV_EUNSUPPORTED"}
 
@@ -52,7 +53,7 @@ _P = ctypes.POINTER
 _SIGS = {
     "pkv_paged_kv_write": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _P(CacheDesc), _vp]),
     "pkv_copy_blocks": (_i32, [_vp, _vp, _P(CacheDesc), _vp, _i32, _vp]),
-    "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pkv_decode_workspace_bytes": (_sz, [_P(CacheDesc), _i32, _i32, _i32, _i32]),
     "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _P(CacheDesc), _vp, _i32, _vp, _i32,
                                           _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pkv_validate_write": (_i32, [_vp, _i32, _P(CacheDesc)]),
@@ -165,20 +166,28 @@ def copy_blocks(k_cache, v_cache, src_dst_pairs, stream=None) -> None:
                                  _ptr(src_dst_pairs), n, _stream(stream)))
 
 
-def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
-                           max_context_len: int, partition_size: int) -> int:
-    return int(lib().pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
-                                                max_context_len, partition_size))
+def decode_workspace_bytes(desc: CacheDesc, num_seqs: int, num_q_heads: int,
+                           max_context_len: int, partition_size: int = PKV_PARTITION_AUTO) -> int:
+    """Workspace bytes a decode with these sizes needs on the current device."""
+    n = int(lib().pkv_decode_workspace_bytes(ctypes.byref(desc), num_seqs, num_q_heads,
+                                             max_context_len, partition_size))
+    if n == 0:
+        err = lib().pkv_last_error().decode()
+        if err:
+            raise PagedKVError(PKV_EINVAL, err)
+    return n
 
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
-                           max_context_len: int, partition_size: int = 512, workspace=None,
-                           stream=None) -> None:
+                           max_context_len: int, partition_size: int = PKV_PARTITION_AUTO,
+                           workspace=None, stream=None) -> None:
     """out, q: [S, Hq, D]; block_tables: [S, M] int32; context_lens: [S] int32.
 
-    ``max_context_len`` is the host-side bound of context_lens.  ``workspace``
-    is a device uint8 tensor of at least decode_workspace_bytes(...) bytes; if
-    None, one is allocated with torch (plumbing, outside the kernels).
+    ``max_context_len`` is the host-side bound of context_lens.
+    ``partition_size``: PKV_PARTITION_AUTO (balanced split), a positive
+    multiple of the block size (split-context partitions) or 0 (no split).
+    ``workspace`` is a device uint8 tensor of at least decode_workspace_bytes(...)
+    bytes; if None, one is allocated with torch (plumbing, outside the kernels).
     """
     torch = _torch()
     S, Hq, D = q.shape
@@ -188,11 +197,12 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         raise PagedKVError(PKV_EINVAL, "block_tables and context_lens must be int32")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
         raise PagedKVError(PKV_EINVAL, "block_tables must be [S, M] and context_lens [S]")
-    need = decode_workspace_bytes(S, Hq, D, max_context_len, partition_size)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     desc = cache_desc(k_cache)
+    if workspace is None and S:
+        need = decode_workspace_bytes(desc, S, Hq, max_context_len, partition_size)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pkv_paged_attention_decode(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
         _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S, Hq,

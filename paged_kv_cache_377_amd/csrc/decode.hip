@@ -351,10 +351,12 @@ __global__ __launch_bounds__(kThreads) void decode_partition_valu_kernel(
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+constexpr int kTile = 16;  // tokens per MFMA tile
+
 // D = A B + C on a 16x16x32 bf16 tile.  Lane l supplies row (l % 16) of A and
 // column (l % 16) of B, each as 8 consecutive k-slots of group l / 16; it
 // receives D[4 (l / 16) + r][l % 16] in element r.  Only the pairing of A's
-// and B's k-slots matters to the kernel, not their order.
+// and B's k-slots matters to the kernels, not their order.
 __device__ inline f32x4_t mfma16x16x32(const uint4& a, const uint4& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -367,10 +369,178 @@ __device__ inline uint32_t pack_bf16_pair(float lo, float hi) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Max / sum over the four 16-lane rows of the wave (lanes with equal l % 16),
+// with the VALU row-swap instructions: after a swap each lane holds its own
+// value and its partner row's value in the two results.
+__device__ inline float rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ inline float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // A tile's maximum must exceed the reference maximum by more than this (log2
 // units) before the accumulators are rescaled; weights stay <= 2^8.
 constexpr float kRescaleSlack = 8.0f;
 
+// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their
+// maxima (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
+constexpr int kWaitVmcnt0 = (7 << 4) | (15 << 8);
+
+// The K and V pieces of the 16 token rows of one tile as one wave holds them:
+// lane (grp = l / 16, col = l % 16) has dims 32 kk + 8 grp .. + 7 of row col.
+template <int D>
+struct KVTile {
+  uint4 k[D / 32], v[D / 32];
+  bool ok;  // this lane's row is live and its block id is inside the pool
+};
+
+// Load row `tok` (offset tok % B of block `phys`, KV head g) into x.  A row
+// that is not live, or whose block id is outside the pool, reads `safe` (a
+// small in-bounds row) instead, and its V is zeroed when it is used.  The
+// loads are never predicated, so the compiler can count them in flight.
+template <int D, int B>
+__device__ inline void load_kv(KVTile<D>& x, const uint16_t* __restrict__ k_cache,
+                               const uint16_t* __restrict__ v_cache, const uint16_t* safe,
+                               bool live, int phys, int tok, int g, int num_kv_heads,
+                               int num_blocks, int grp) {
+  x.ok = live && phys >= 0 && phys < num_blocks;
+  const int64_t off = ((int64_t)phys * num_kv_heads + g) * (B * D) + (int64_t)(tok % B) * D + 8 * grp;
+  const uint16_t* kp = x.ok ? k_cache + off : safe;
+  const uint16_t* vp = x.ok ? v_cache + off : safe;
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    x.k[kk] = *reinterpret_cast<const uint4*>(kp + 32 * kk);
+    x.v[kk] = *reinterpret_cast<const uint4*>(vp + 32 * kk);
+  }
+}
+
+// One wave's online-softmax state for the G query heads of one KV head and its
+// update by one tile on the matrix cores (v_mfma_f32_16x16x32_bf16):
+//   * scores: A = the 16 K rows (tokens), B = the group's query rows (columns
+//     = heads, zero past G); lane (grp, col) receives the scores of tokens
+//     4 grp + r for head col;
+//   * V^T: V is token-major but the output product contracts over tokens, so
+//     each 16x16 tile of V is transposed by a product with a 0/1 selection
+//     matrix (exact: one non-zero term per output);
+//   * output: A = V^T tile (rows = 16 dims), B = P (columns = heads) with P
+//     split into a bf16 high part and a bf16 low part (both in the contraction)
+//     so the weights keep ~16 significant bits.
+// The output tile of a head lands in the lanes that hold that head's softmax
+// statistics, so rescaling needs no data exchange.
+template <int D, int G>
+struct MfmaAttn {
+  static constexpr int KP = D / 32;  // 32-dim pieces of a row
+  static constexpr int DT = D / 16;  // 16-dim output tiles
+  static_assert(D % 32 == 0 && G >= 1 && G <= 16, "unsupported shape");
+  uint4 qb[KP];   // B operand of the scores: q[head col][dims 32 kk + 8 grp ..]
+  uint4 sel[2];   // selection matrices of the V transposes
+  f32x4_t o[DT];  // o[j][r] = unnormalised output, head col, dim 16 j + 4 grp + r
+  float m;        // reference maximum of head col (log2 units)
+  float l;        // this lane's share of the weight sum of head col
+
+  __device__ void init(int col, int grp) {
+    // column c of half h picks dim 16 h + c of a 32-dim piece, i.e. k-slot
+    // (2 h + c / 8, c % 8).  bf16 1.0 = 0x3f80.
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bool on = grp == 2 * h + (col >> 3);
+      const int e = col & 7;
+      const uint32_t one = 0x3f80u << (16 * (e & 1));
+      sel[h] = make_uint4(on && (e >> 1) == 0 ? one : 0u, on && (e >> 1) == 1 ? one : 0u,
+                          on && (e >> 1) == 2 ? one : 0u, on && (e >> 1) == 3 ? one : 0u);
+    }
+    reset();
+  }
+
+  __device__ void reset() {
+#pragma unroll
+    for (int j = 0; j < DT; ++j) o[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    m = -INFINITY;
+    l = 0.0f;
+  }
+
+  // qgroup = q row of the group's first head.  k-slot (grp, e) of piece kk is
+  // dim 32 kk + 8 grp + e for K rows and q alike.  Columns past the group's G
+  // heads are zero (their lanes read the first head's row).
+  __device__ void load_q(const uint16_t* qgroup, int col, int grp) {
+    const uint16_t* qrow = qgroup + (col < G ? col : 0) * D + 8 * grp;
+#pragma unroll
+    for (int kk = 0; kk < KP; ++kk) {
+      const uint4 x = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
+      qb[kk] = col < G ? x : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  // Rows 0 .. nvalid - 1 of the tile count (1 <= nvalid <= 16); later rows
+  // are masked, whatever their K and V bits.
+  __device__ void update(KVTile<D>& x, int nvalid, float qscale, int grp) {
+    // V rows that do not count become zeros (their weight is 0, and 0 * NaN
+    // would otherwise poison the output)
+#pragma unroll
+    for (int kk = 0; kk < KP; ++kk)
+      if (!x.ok) x.v[kk] = make_uint4(0, 0, 0, 0);
+    // V^T tiles first: they do not depend on the scores, so these products
+    // overlap the score products and the softmax arithmetic.
+    // va[j] = bf16 pairs of V[token 4 grp + r][dim 16 j + col], r = 0..3
+    uint32_t va[DT][2];
+#pragma unroll
+    for (int j = 0; j < DT; ++j) {
+      const f32x4_t tv = mfma16x16x32(x.v[j >> 1], sel[j & 1], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
+      va[j][0] = pack_bf16_pair(tv[0], tv[1]);
+      va[j][1] = pack_bf16_pair(tv[2], tv[3]);
+    }
+    f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < KP; ++kk) sc = mfma16x16x32(x.k[kk], qb[kk], sc);
+    float sv[4];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sv[r] = 4 * grp + r < nvalid ? sc[r] * qscale : -INFINITY;
+      bm = fmaxf(bm, sv[r]);
+    }
+    bm = rows_max(bm);  // maximum over the tile's tokens
+    const bool need = bm > m + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float alpha = need ? fast_exp2(m - bm) : 1.0f;  // 0 on the first tile
+      m = need ? bm : m;
+      l *= alpha;
+#pragma unroll
+      for (int j = 0; j < DT; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[j][r] *= alpha;
+    }
+    float pw[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pw[r] = fast_exp2(sv[r] - m);  // masked rows: exactly 0
+    l += (pw[0] + pw[1]) + (pw[2] + pw[3]);
+    // P as the B operand: k-slots e < 4 hold the bf16 high parts of the
+    // weights of tokens 4 grp + e, slots e >= 4 the rounded remainders.
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      hi[r] = __float_as_uint(pw[r]) & 0xffff0000u;
+      lo[r] = (__float_as_uint(pw[r] - __uint_as_float(hi[r])) + 0x8000u) & 0xffff0000u;
+    }
+    const uint4 pb = make_uint4((hi[0] >> 16) | hi[1], (hi[2] >> 16) | hi[3],
+                                (lo[0] >> 16) | lo[1], (lo[2] >> 16) | lo[3]);
+    // o[j] element r += sum_t V[t][dim 16 j + 4 grp + r] * P[t][head col]
+#pragma unroll
+    for (int j = 0; j < DT; ++j)
+      o[j] = mfma16x16x32(make_uint4(va[j][0], va[j][1], va[j][0], va[j][1]), pb, o[j]);
+  }
+};
+
+// Split-context kernel for bf16 caches: one workgroup per (partition,
+// sequence, KV head), block-table entries of the partition staged in LDS.
 template <int D, int B, int G>
 __global__ __launch_bounds__(kThreads) void decode_partition_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
@@ -379,12 +549,9 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_kernel(
     float* __restrict__ part_ml, float* __restrict__ part_o, int32_t num_seqs,
     int32_t num_kv_heads, int32_t num_blocks, int32_t num_parts, int32_t ps,
     int32_t max_context_len, float qscale) {
-  constexpr int KP = D / 32;           // 32-dim pieces of a row: one 16-byte load per lane each
-  constexpr int DT = D / 16;           // 16-dim output tiles
-  constexpr int kTile = 16;            // tokens per MFMA tile
+  constexpr int DT = D / 16;
   constexpr int kChunkTiles = 64;      // tiles whose table entries are staged at once
   constexpr int kChunkEntries = kChunkTiles * kTile / B + 2;
-  static_assert(D % 32 == 0 && G >= 1 && G <= 16, "unsupported shape");
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -416,31 +583,9 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_kernel(
   const int ntiles = (t1 - t0 + kTile - 1) / kTile;
   const int nparts_s = (n + ps - 1) / ps;
 
-  // k-slot (grp, e) of piece kk is dim 32 kk + 8 grp + e, for K rows and q alike.
-  uint4 qb[KP];
-#pragma unroll
-  for (int kk = 0; kk < KP; ++kk)
-    qb[kk] = col < G ? *reinterpret_cast<const uint4*>(q + ((int64_t)s * hq + g * G + col) * D +
-                                                       32 * kk + 8 * grp)
-                     : make_uint4(0, 0, 0, 0);
-
-  // Selection matrices: column c of half h picks dim 16 h + c of a 32-dim
-  // piece, i.e. k-slot (2 h + c / 8, c % 8).  bf16 1.0 = 0x3f80.
-  uint4 sel[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const bool on = grp == 2 * h + (col >> 3);
-    const int e = col & 7;
-    const uint32_t one = 0x3f80u << (16 * (e & 1));
-    sel[h] = make_uint4(on && (e >> 1) == 0 ? one : 0u, on && (e >> 1) == 1 ? one : 0u,
-                        on && (e >> 1) == 2 ? one : 0u, on && (e >> 1) == 3 ? one : 0u);
-  }
-
-  f32x4_t o[DT];
-#pragma unroll
-  for (int j = 0; j < DT; ++j) o[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  float m = -INFINITY;  // reference maximum of head `col` (log2 units)
-  float l = 0.0f;       // this lane's share of the weight sum of head `col`
+  MfmaAttn<D, G> at;
+  at.init(col, grp);
+  at.load_q(q + ((int64_t)s * hq + g * G) * D, col, grp);
 
   __shared__ int32_t sm_bt[kChunkEntries];
   __shared__ float sm_m[kWaves][G];
@@ -448,89 +593,14 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_kernel(
   __shared__ float sm_o[kWaves][G][D];
 
   const int32_t* bt = block_tables + (int64_t)s * table_width;
-  const int64_t blk_stride = (int64_t)num_kv_heads * B * D;
-  const int64_t head_off = (int64_t)g * B * D + 8 * grp;
+  const uint16_t* safe = q + 8 * grp;
 
-  // The K and V pieces of token row `col` of a tile.  The loads are not
-  // predicated, so the compiler can keep the next tile's loads in flight
-  // while the current tile is processed: a row past the partition (or whose
-  // block id is outside the pool) reads this lane's query piece instead, a
-  // small in-bounds row, and its V is replaced by zeros when it is used.
-  const uint16_t* q_safe = q + ((int64_t)s * hq + g * G) * D + 8 * grp;
-  struct Tile {
-    uint4 k[KP], v[KP];
-    bool ok;
-  };
-  auto load_tile = [&](int tile, int cb0, Tile& x) {
+  auto load_tile = [&](int tile, int cb0, KVTile<D>& x) {
     const int t = t0 + tile * kTile + col;
     const bool live = tile >= 0 && t < t1;
     const int tc = live ? t : t1 - 1;  // stays inside the staged chunk
-    const int phys = sm_bt[tc / B - cb0];
-    x.ok = live && phys >= 0 && phys < num_blocks;
-    const int64_t off = (int64_t)phys * blk_stride + head_off + (int64_t)(tc % B) * D;
-    const uint16_t* kp = x.ok ? k_cache + off : q_safe;
-    const uint16_t* vp = x.ok ? v_cache + off : q_safe;
-#pragma unroll
-    for (int kk = 0; kk < KP; ++kk) {
-      x.k[kk] = *reinterpret_cast<const uint4*>(kp + 32 * kk);
-      x.v[kk] = *reinterpret_cast<const uint4*>(vp + 32 * kk);
-    }
-  };
-
-  auto process = [&](int tile, Tile& x) {
-    // scores of tokens 4 grp + r (tile rows) for head `col`; rows that are
-    // not live are replaced by -inf below, whatever their K bits were
-    f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int kk = 0; kk < KP; ++kk) sc = mfma16x16x32(x.k[kk], qb[kk], sc);
-    // V rows that are not live become zeros (their weight is 0, and 0 * NaN
-    // would otherwise poison the output)
-#pragma unroll
-    for (int kk = 0; kk < KP; ++kk)
-      if (!x.ok) x.v[kk] = make_uint4(0, 0, 0, 0);
-    const int tb = t0 + tile * kTile + 4 * grp;
-    float sv[4];
-    float bm = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sv[r] = tb + r < t1 ? sc[r] * qscale : -INFINITY;
-      bm = fmaxf(bm, sv[r]);
-    }
-    bm = fmaxf(bm, xor16(bm));
-    bm = fmaxf(bm, xor32(bm));  // maximum over the tile's 16 tokens
-    const bool need = bm > m + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float alpha = need ? fast_exp2(m - bm) : 1.0f;  // 0 on the first tile
-      m = need ? bm : m;
-      l *= alpha;
-#pragma unroll
-      for (int j = 0; j < DT; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[j][r] *= alpha;
-    }
-    float pw[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pw[r] = fast_exp2(sv[r] - m);  // masked rows: exactly 0
-    l += (pw[0] + pw[1]) + (pw[2] + pw[3]);
-    // P as the B operand: k-slots e < 4 hold the bf16 high parts of the
-    // weights of tokens 4 grp + e, slots e >= 4 the rounded remainders.
-    uint32_t hi[4], lo[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      hi[r] = __float_as_uint(pw[r]) & 0xffff0000u;
-      lo[r] = (__float_as_uint(pw[r] - __uint_as_float(hi[r])) + 0x8000u) & 0xffff0000u;
-    }
-    const uint4 pb = make_uint4((hi[0] >> 16) | hi[1], (hi[2] >> 16) | hi[3],
-                                (lo[0] >> 16) | lo[1], (lo[2] >> 16) | lo[3]);
-#pragma unroll
-    for (int j = 0; j < DT; ++j) {
-      // V^T tile j: element r = V[token 4 grp + r][dim 16 j + col], exact
-      const f32x4_t tv = mfma16x16x32(x.v[j >> 1], sel[j & 1], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
-      const uint32_t a01 = pack_bf16_pair(tv[0], tv[1]);
-      const uint32_t a23 = pack_bf16_pair(tv[2], tv[3]);
-      // o[j] element r += sum_t V[t][dim 16 j + 4 grp + r] * P[t][head col]
-      o[j] = mfma16x16x32(make_uint4(a01, a23, a01, a23), pb, o[j]);
-    }
+    load_kv<D, B>(x, k_cache, v_cache, safe, live, sm_bt[tc / B - cb0], tc, g, num_kv_heads,
+                  num_blocks, grp);
   };
 
   for (int c0 = 0; c0 < ntiles; c0 += kChunkTiles) {
@@ -542,39 +612,234 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_kernel(
     __syncthreads();
     int tile = c0 + wave;
     if (tile >= c1) continue;
-    // Two tile buffers in turn: the loads of the tile after the current one
-    // (or of a dummy row past the chunk's end) are issued before the current
-    // tile is processed.
-    Tile ta, tb;
+    // Nothing but the tile loads below may be in flight when the loop is
+    // entered, so the compiler can count them precisely (vmcnt) in the loop.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    // Two tile buffers in turn: the loads of the next tile (or of dummy rows)
+    // are issued before the current tile is processed.  The wave's tile count
+    // is padded to an even number so the loop has a single exit, which keeps
+    // the compiler's load counting exact across the back edge.
+    const int mine = (c1 - 1 - tile) / kWaves + 1;
+    KVTile<D> ta, tb;
     load_tile(tile, cb0, ta);
-    for (;;) {
-      load_tile(tile + kWaves < c1 ? tile + kWaves : -1, cb0, tb);
-      process(tile, ta);
-      tile += kWaves;
-      if (tile >= c1) break;
-      load_tile(tile + kWaves < c1 ? tile + kWaves : -1, cb0, ta);
-      process(tile, tb);
-      tile += kWaves;
-      if (tile >= c1) break;
+    for (int it = 0; it < (mine + 1) / 2; ++it, tile += 2 * kWaves) {
+      const int t_b = tile + kWaves;
+      const int t_c = tile + 2 * kWaves;
+      load_tile(t_b < c1 ? t_b : -1, cb0, tb);
+      at.update(ta, min(kTile, t1 - (t0 + tile * kTile)), qscale, grp);
+      load_tile(t_c < c1 ? t_c : -1, cb0, ta);
+      if (t_b < c1) at.update(tb, min(kTile, t1 - (t0 + t_b * kTile)), qscale, grp);
     }
   }
 
   // the four row groups of a head hold disjoint tokens' weight sums
-  l += xor16(l);
-  l += xor32(l);
+  const float l = rows_sum(at.l);
   if (grp == 0 && col < G) {
-    sm_m[wave][col] = m;
+    sm_m[wave][col] = at.m;
     sm_l[wave][col] = l;
   }
   if (col < G) {
 #pragma unroll
     for (int j = 0; j < DT; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm_o[wave][col][16 * j + 4 * grp + r] = o[j][r];
+      for (int r = 0; r < 4; ++r) sm_o[wave][col][16 * j + 4 * grp + r] = at.o[j][r];
   }
   __syncthreads();
   merge_waves<uint16_t, D, G>(sm_m, sm_l, sm_o, (int64_t)s * hq + g * G, p, num_parts, nparts_s,
                               out, part_ml, part_o);
+}
+
+// ------------------------------------------------------ balanced (bf16)
+//
+// The work is the list of all 16-token tiles of all (sequence, KV head) pairs,
+// numbered pair by pair (sequence, then KV head, then tile).  Each wave is a
+// worker that takes one contiguous, equal share [w T / nw, (w + 1) T / nw) of
+// the T tiles, so every worker reads the same number of K/V bytes however
+// ragged the context lengths are, and streams its share with the next tiles'
+// loads always in flight.  nw = min(T, NW), NW being the number of waves the
+// GPU holds at once.
+// A worker's share cuts the pair list into segments; for each segment the
+// worker either writes the finished output (it holds the whole pair) or a
+// partial (m, l, o) to slot (pair + w), and the worker holding a pair's first
+// tile records which workers cover the pair.  Slots are distinct: along the
+// tile list, pair + worker grows by at least one at every segment start.
+
+// Number of the worker whose share [w T / nw, (w + 1) T / nw) holds tile u.
+__device__ inline int worker_of(int64_t u, int64_t total, int32_t num_workers) {
+  return (int)(((u + 1) * num_workers - 1) / total);
+}
+
+template <int D, int B, int G>
+__global__ __launch_bounds__(kThreads) void decode_balanced_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
+    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
+    int32_t table_width, const int32_t* __restrict__ context_lens, uint16_t* __restrict__ out,
+    int2* __restrict__ meta, float* __restrict__ part_ml, float* __restrict__ part_o,
+    int32_t num_seqs, int32_t num_kv_heads, int32_t num_blocks, int32_t max_context_len,
+    int32_t num_workers, float qscale) {
+  constexpr int DT = D / 16;
+  extern __shared__ int32_t sm_dyn[];
+  int32_t* sm_c = sm_dyn;                 // [num_seqs + 1] tiles of one KV head before sequence s
+  int32_t* sm_n = sm_dyn + num_seqs + 1;  // [num_seqs] clamped context lengths
+  __shared__ int32_t sm_scan[kThreads];
+
+  // Prefix sums of the tile counts (every workgroup computes its own copy).
+  {
+    const int per = (num_seqs + kThreads - 1) / kThreads;
+    const int i0 = min(num_seqs, (int)threadIdx.x * per);
+    const int i1 = min(num_seqs, i0 + per);
+    int local = 0;
+    for (int i = i0; i < i1; ++i) {
+      // Lengths outside [0, max_context_len] break the caller's contract;
+      // clamping keeps every access in bounds regardless.
+      const int n = min(max(context_lens[i], 0), max_context_len);
+      sm_n[i] = n;
+      local += (n + kTile - 1) / kTile;
+    }
+    sm_scan[threadIdx.x] = local;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+      const int v = (int)threadIdx.x >= off ? sm_scan[threadIdx.x - off] : 0;
+      __syncthreads();
+      sm_scan[threadIdx.x] += v;
+      __syncthreads();
+    }
+    int run = sm_scan[threadIdx.x] - local;
+    for (int i = i0; i < i1; ++i) {
+      sm_c[i] = run;
+      run += (sm_n[i] + kTile - 1) / kTile;
+    }
+    if (threadIdx.x == kThreads - 1) sm_c[num_seqs] = sm_scan[kThreads - 1];
+    __syncthreads();
+  }
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int hq = num_kv_heads * G;
+  const int64_t total = (int64_t)num_kv_heads * sm_c[num_seqs];
+  // With fewer tiles than workers only the first `total` workers take one
+  // each: every worker in [0, nw) has a non-empty share, so the workers that
+  // cover a pair are exactly the range between its first and last tile's.
+  const int nw = (int)min((int64_t)num_workers, total);
+  const int w = blockIdx.x * kWaves + wave;
+  if (w >= nw) return;  // no barrier follows: the waves are independent from here
+  const int64_t u0 = (int64_t)w * total / nw;
+  const int64_t u1 = (int64_t)(w + 1) * total / nw;
+
+  // A tile's place: sequence, KV head, tile index in the pair, the pair's tile
+  // count and the sequence's length (all wave-uniform).
+  struct Pos {
+    int s, g, tile, nt, n;
+  };
+  auto seq_info = [&](Pos& x) {
+    x.nt = __builtin_amdgcn_readfirstlane(sm_c[x.s + 1] - sm_c[x.s]);
+    x.n = __builtin_amdgcn_readfirstlane(sm_n[x.s]);
+  };
+  auto pos_of = [&](int64_t u) {
+    int lo = 0, hi = num_seqs - 1;  // last sequence whose first tile is <= u
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int64_t)num_kv_heads * sm_c[mid] <= u) lo = mid; else hi = mid - 1;
+    }
+    Pos x;
+    x.s = __builtin_amdgcn_readfirstlane(lo);
+    seq_info(x);
+    const int64_t r = u - (int64_t)num_kv_heads * __builtin_amdgcn_readfirstlane(sm_c[x.s]);
+    x.g = (int)(r / x.nt);
+    x.tile = (int)(r - (int64_t)x.g * x.nt);
+    return x;
+  };
+  auto next = [&](Pos x) {  // only called for tiles before u1, so the result is a tile
+    if (++x.tile < x.nt) return x;
+    x.tile = 0;
+    if (++x.g < num_kv_heads) return x;
+    x.g = 0;
+    do {
+      ++x.s;
+    } while (__builtin_amdgcn_readfirstlane(sm_c[x.s + 1]) == __builtin_amdgcn_readfirstlane(sm_c[x.s]));
+    seq_info(x);
+    return x;
+  };
+  // Block-table entry of this lane's row of tile x (a valid entry of the
+  // sequence's row even for rows past its end).
+  auto table_entry = [&](const Pos& x) {
+    const int t = min(x.tile * kTile + col, x.n - 1);
+    return block_tables[(int64_t)x.s * table_width + t / B];
+  };
+  const uint16_t* safe = q + 8 * grp;
+  auto load_tile = [&](const Pos& x, int phys, bool live, KVTile<D>& kv) {
+    const int t = x.tile * kTile + col;
+    load_kv<D, B>(kv, k_cache, v_cache, safe, live && t < x.n, phys, t, x.g, num_kv_heads,
+                  num_blocks, grp);
+  };
+
+  MfmaAttn<D, G> at;
+  at.init(col, grp);
+  int64_t seg_u0 = u0;  // first tile of the current segment
+
+  // Update with tile u (place x); at the end of a segment write its result
+  // and prepare for the next pair (place nx).
+  auto step = [&](const Pos& x, int64_t u, KVTile<D>& kv, const Pos& nx) {
+    at.update(kv, min(kTile, x.n - x.tile * kTile), qscale, grp);
+    if (x.tile + 1 < x.nt && u + 1 < u1) return;
+    const int64_t pair_u0 = (int64_t)num_kv_heads * sm_c[x.s] + (int64_t)x.g * x.nt;
+    const int pair = x.s * num_kv_heads + x.g;
+    const bool first = seg_u0 == pair_u0;
+    const bool whole = first && u + 1 == pair_u0 + x.nt;
+    const float l = rows_sum(at.l);
+    if (col < G) {
+      const int64_t row = (int64_t)x.s * hq + x.g * G + col;
+      if (whole) {
+#pragma unroll
+        for (int j = 0; j < DT; ++j) {
+          uint2 v;
+          v.x = (uint32_t)f32_to_bf16_rne(at.o[j][0] / l) |
+                ((uint32_t)f32_to_bf16_rne(at.o[j][1] / l) << 16);
+          v.y = (uint32_t)f32_to_bf16_rne(at.o[j][2] / l) |
+                ((uint32_t)f32_to_bf16_rne(at.o[j][3] / l) << 16);
+          *reinterpret_cast<uint2*>(out + row * D + 16 * j + 4 * grp) = v;
+        }
+      } else {
+        const int64_t slot = ((int64_t)pair + w) * G + col;
+#pragma unroll
+        for (int j = 0; j < DT; ++j)
+          *reinterpret_cast<float4*>(part_o + slot * D + 16 * j + 4 * grp) =
+              make_float4(at.o[j][0], at.o[j][1], at.o[j][2], at.o[j][3]);
+        if (grp == 0) *reinterpret_cast<float2*>(part_ml + slot * 2) = make_float2(at.m, l);
+      }
+    }
+    if (first && lane == 0)
+      meta[pair] = make_int2(w, worker_of(pair_u0 + x.nt - 1, total, nw));
+    if (u + 1 < u1) {
+      at.reset();
+      at.load_q(q + ((int64_t)nx.s * hq + nx.g * G) * D, col, grp);
+      seg_u0 = u + 1;
+    }
+  };
+
+  // Pipeline: the table entry of tile u + 2 and the K/V of tile u + 1 are in
+  // flight while tile u is processed; two tile buffers in turn, with the tile
+  // count padded to an even number (a dummy tile) so the loop has one exit.
+  Pos pa = pos_of(u0);
+  at.load_q(q + ((int64_t)pa.s * hq + pa.g * G) * D, col, grp);
+  Pos pb = u0 + 1 < u1 ? next(pa) : pa;
+  int ph_b = table_entry(pb);
+  KVTile<D> ta, tb;
+  load_tile(pa, table_entry(pa), true, ta);
+  for (int64_t u = u0; u < u1; u += 2) {
+    const Pos pc = u + 2 < u1 ? next(pb) : pb;
+    const int ph_c = table_entry(pc);
+    load_tile(pb, ph_b, u + 1 < u1, tb);
+    step(pa, u, ta, pb);
+    const Pos pd = u + 3 < u1 ? next(pc) : pc;
+    ph_b = table_entry(pd);
+    load_tile(pc, ph_c, u + 2 < u1, ta);
+    if (u + 1 < u1) step(pb, u + 1, tb, pc);
+    pa = pc;
+    pb = pd;
+  }
 }
 
 // --------------------------------------------------------------- reduce
@@ -605,7 +870,155 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(
   store_out(out + row * D + d, O / L);
 }
 
+// One wave per (pair, query head) of the balanced split: pairs covered by
+// several workers are combined here, in worker order,
+// out = sum_w o_w 2^(m_w - m*) / sum_w L_w 2^(m_w - m*); heads of empty
+// sequences get zeros; pairs finished by a single worker are left alone.
+// The lanes first fold the workers' (m, L) in parallel (fixed butterfly
+// order), then walk the workers' output rows with D / 64 dims per lane.
+template <int D, int G>
+__global__ __launch_bounds__(kWave) void decode_balanced_reduce_kernel(
+    uint16_t* __restrict__ out, const int2* __restrict__ meta, const float* __restrict__ part_ml,
+    const float* __restrict__ part_o, const int32_t* __restrict__ context_lens,
+    int32_t num_kv_heads, int32_t max_context_len, int32_t num_workers) {
+  constexpr int DPL = D / kWave;  // dims per lane
+  constexpr int kUnroll = 8;
+  static_assert(DPL * kWave == D, "head_dim must be a multiple of 64");
+  const int pair = blockIdx.x / G;
+  const int h = blockIdx.x - pair * G;
+  const int lane = threadIdx.x;
+  const int s = pair / num_kv_heads;
+  uint16_t* orow = out + ((int64_t)pair * G + h) * D + lane * DPL;
+  const int n = min(max(context_lens[s], 0), max_context_len);
+  if (n == 0) {
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) store_out(orow + e, 0.0f);
+    return;
+  }
+  const int2 mt = meta[pair];
+  const int wa = max(mt.x, 0), wb = min(mt.y, num_workers - 1);
+  if (wa >= wb) return;
+  const int nseg = wb - wa + 1;
+  const float* ml = part_ml + (((int64_t)pair + wa) * G + h) * 2;  // worker k at ml[k * 2 G]
+  const float* po = part_o + (((int64_t)pair + wa) * G + h) * D + lane * DPL;
+
+  // (max, sum) over this lane's workers k = lane, lane + 64, ...
+  float M = -INFINITY, L = 0.0f;
+  for (int k = lane; k < nseg; k += kWave) {
+    const float2 v = *reinterpret_cast<const float2*>(ml + (int64_t)k * 2 * G);
+    const float mx = fmaxf(M, v.x);
+    L = L * (M == -INFINITY ? 0.0f : exp2f(M - mx)) + v.y * exp2f(v.x - mx);
+    M = mx;
+  }
+  // butterfly over the wave: every lane ends with the same bits
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const float om = __shfl_xor(M, off, kWave);
+    const float ol = __shfl_xor(L, off, kWave);
+    const float mx = fmaxf(M, om);
+    const float a = M == -INFINITY ? 0.0f : L * exp2f(M - mx);
+    const float b = om == -INFINITY ? 0.0f : ol * exp2f(om - mx);
+    L = (lane & off) ? b + a : a + b;
+    M = mx;
+  }
+  float O[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) O[e] = 0.0f;
+  for (int k0 = 0; k0 < nseg; k0 += kUnroll) {
+    float mv[kUnroll], ov[kUnroll][DPL];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int k = min(k0 + u, nseg - 1);
+      mv[u] = ml[(int64_t)k * 2 * G];
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) ov[u][e] = po[(int64_t)k * G * D + e];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (k0 + u < nseg) {
+        const float f = exp2f(mv[u] - M);
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) O[e] = fmaf(ov[u][e], f, O[e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) store_out(orow + e, O[e] / L);
+}
+
 // ------------------------------------------------------------- dispatch
+
+constexpr int kMaxSeqsBalanced = 8191;  // prefix sums and lengths fit 64 KiB of LDS
+constexpr int kWorkerWavesPerSimd = 2;  // the balanced kernel's occupancy (VGPR-bound)
+
+// How one call is split and where its workspace pieces go.
+struct Plan {
+  bool balanced;
+  int32_t parts;    // split-context: partitions per sequence
+  int32_t ps;       // split-context: tokens per partition
+  int32_t workers;  // balanced: workers (waves)
+  size_t meta_off, ml_off, o_off, bytes;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workers of the balanced split: the waves the current device holds at once.
+int workers_for_device(int32_t* nw) {
+  static int cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return pkv__fail(PKV_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
+    *nw = cache[dev];
+    return PKV_OK;
+  }
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess || cus <= 0)
+    return pkv__fail(PKV_EHIP, "compute unit count: %s", hipGetErrorString(e));
+  *nw = cus * 4 * kWorkerWavesPerSimd;
+  if (dev >= 0 && dev < 64) cache[dev] = *nw;
+  return PKV_OK;
+}
+
+int make_plan(const pkv_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
+              int32_t max_context_len, int32_t partition_size, Plan* pl) {
+  const int32_t B = c->block_size, D = c->head_dim;
+  const int32_t G = num_q_heads / c->num_kv_heads;
+  *pl = Plan{};
+  if (partition_size == PKV_PARTITION_AUTO) {
+    const int64_t tiles_per_head = (int64_t)num_seqs * ((max_context_len + kTile - 1) / kTile);
+    if (c->dtype == PKV_BF16 && num_seqs <= kMaxSeqsBalanced && tiles_per_head < (1 << 30)) {
+      int32_t nw = 0;
+      int rc = workers_for_device(&nw);
+      if (rc) return rc;
+      const size_t pairs = (size_t)num_seqs * c->num_kv_heads;
+      const size_t slots = (pairs + (size_t)nw) * G;
+      pl->balanced = true;
+      pl->workers = nw;
+      pl->meta_off = 0;
+      pl->ml_off = align256(pairs * sizeof(int2));
+      pl->o_off = pl->ml_off + align256(slots * 2 * sizeof(float));
+      pl->bytes = pl->o_off + slots * (size_t)D * sizeof(float);
+      return PKV_OK;
+    }
+    partition_size = 512;  // a multiple of every compiled block size
+  }
+  const int32_t parts = (partition_size <= 0 || max_context_len <= 0)
+                            ? 1
+                            : (max_context_len + partition_size - 1) / partition_size;
+  pl->parts = parts;
+  // With no split, one partition holds the longest context.
+  pl->ps = parts == 1 ? (max_context_len > 0 ? ((max_context_len + B - 1) / B) * B : B)
+                      : partition_size;
+  if (parts > 1) {
+    const size_t rows = (size_t)num_seqs * num_q_heads * parts;
+    pl->ml_off = 0;
+    pl->o_off = rows * 2 * sizeof(float);
+    pl->bytes = pl->o_off + rows * (size_t)D * sizeof(float);
+  }
+  return PKV_OK;
+}
 
 struct LaunchArgs {
   void* out;
@@ -620,41 +1033,65 @@ struct LaunchArgs {
   int32_t num_blocks;
   int32_t max_context_len;
   int32_t num_q_heads;
-  int32_t num_parts;
-  int32_t ps;
+  Plan plan;
   float qscale;
+  int2* meta;
   float* part_ml;
   float* part_o;
   hipStream_t stream;
 };
 
+int check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return pkv__fail(PKV_EHIP, "%s launch: %s", what, hipGetErrorString(e));
+  return PKV_OK;
+}
+
 template <typename E, int D, int B, int G>
 int launch(const LaunchArgs& a) {
-  const int64_t grid = (int64_t)a.num_seqs * a.num_kv_heads * a.num_parts;
+  if constexpr (E::bytes == 2) {
+    if (a.plan.balanced) {
+      const size_t lds = (size_t)(2 * a.num_seqs + 1) * sizeof(int32_t);
+      hipLaunchKernelGGL((decode_balanced_kernel<D, B, G>), dim3((uint32_t)(a.plan.workers / kWaves)),
+                         dim3(kThreads), lds, a.stream, (const uint16_t*)a.q,
+                         (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.block_tables,
+                         a.width, a.context_lens, (uint16_t*)a.out, a.meta, a.part_ml, a.part_o,
+                         a.num_seqs, a.num_kv_heads, a.num_blocks, a.max_context_len,
+                         a.plan.workers, a.qscale);
+      int rc = check_launch("decode_balanced");
+      if (rc) return rc;
+      hipLaunchKernelGGL((decode_balanced_reduce_kernel<D, G>),
+                         dim3((uint32_t)(a.num_seqs * a.num_kv_heads * G)), dim3(kWave), 0, a.stream,
+                         (uint16_t*)a.out, (const int2*)a.meta, (const float*)a.part_ml,
+                         (const float*)a.part_o, a.context_lens, a.num_kv_heads, a.max_context_len,
+                         a.plan.workers);
+      return check_launch("decode_balanced_reduce");
+    }
+  }
+  const int64_t grid = (int64_t)a.num_seqs * a.num_kv_heads * a.plan.parts;
   if (grid > INT32_MAX) return pkv__fail(PKV_EINVAL, "decode grid too large");
   if constexpr (E::bytes == 2) {
     hipLaunchKernelGGL((decode_partition_mfma_kernel<D, B, G>), dim3((uint32_t)grid),
                        dim3(kThreads), 0, a.stream, (const uint16_t*)a.q,
                        (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.block_tables,
                        a.width, a.context_lens, (uint16_t*)a.out, a.part_ml, a.part_o,
-                       a.num_seqs, a.num_kv_heads, a.num_blocks, a.num_parts, a.ps, a.max_context_len,
-                       a.qscale);
+                       a.num_seqs, a.num_kv_heads, a.num_blocks, a.plan.parts, a.plan.ps,
+                       a.max_context_len, a.qscale);
   } else {
     hipLaunchKernelGGL((decode_partition_valu_kernel<E, D, B, G>), dim3((uint32_t)grid),
                        dim3(kThreads), 0, a.stream, (const typename E::raw*)a.q,
                        (const uint4*)a.k_cache, (const uint4*)a.v_cache, a.block_tables,
                        a.width, a.context_lens, (typename E::raw*)a.out, a.part_ml, a.part_o,
-                       a.num_seqs, a.num_kv_heads, a.num_blocks, a.num_parts, a.ps, a.max_context_len,
-                       a.qscale);
+                       a.num_seqs, a.num_kv_heads, a.num_blocks, a.plan.parts, a.plan.ps,
+                       a.max_context_len, a.qscale);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return pkv__fail(PKV_EHIP, "decode_partition launch: %s", hipGetErrorString(e));
-  if (a.num_parts > 1) {
+  int rc = check_launch("decode_partition");
+  if (rc) return rc;
+  if (a.plan.parts > 1) {
     hipLaunchKernelGGL((decode_reduce_kernel<E, D>), dim3((uint32_t)(a.num_seqs * a.num_q_heads)),
                        dim3(D), 0, a.stream, (typename E::raw*)a.out, a.part_ml, a.part_o,
-                       a.context_lens, a.num_q_heads, a.num_parts, a.ps, a.max_context_len);
-    e = hipGetLastError();
-    if (e != hipSuccess) return pkv__fail(PKV_EHIP, "decode_reduce launch: %s", hipGetErrorString(e));
+                       a.context_lens, a.num_q_heads, a.plan.parts, a.plan.ps, a.max_context_len);
+    return check_launch("decode_reduce");
   }
   return PKV_OK;
 }
@@ -689,26 +1126,37 @@ int dispatch_d(const LaunchArgs& a, int D, int B, int G) {
   return pkv__fail(PKV_EUNSUPPORTED, "head_dim %d (compiled: 64, 128)", D);
 }
 
-int32_t parts_for(int32_t max_context_len, int32_t partition_size) {
-  if (partition_size <= 0 || max_context_len <= 0) return 1;
-  return (max_context_len + partition_size - 1) / partition_size;
-}
-
-size_t workspace_for(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t parts) {
-  if (parts <= 1) return 0;
-  return (size_t)num_seqs * num_q_heads * parts * (2 + head_dim) * sizeof(float);
-}
-
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_sizes(const pkv_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
+                int32_t max_context_len, int32_t partition_size) {
+  int rc = pkv__check_desc(c);
+  if (rc) return rc;
+  if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0)
+    return pkv__fail(PKV_EINVAL, "bad sizes (num_seqs=%d num_q_heads=%d max_context_len=%d)",
+                     num_seqs, num_q_heads, max_context_len);
+  if (num_q_heads % c->num_kv_heads != 0)
+    return pkv__fail(PKV_EINVAL, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                     num_q_heads, c->num_kv_heads);
+  if (partition_size != PKV_PARTITION_AUTO &&
+      (partition_size < 0 || (partition_size > 0 && partition_size % c->block_size != 0)))
+    return pkv__fail(PKV_EINVAL,
+                     "partition_size %d must be PKV_PARTITION_AUTO, 0 or a positive multiple of "
+                     "block_size %d", partition_size, c->block_size);
+  return PKV_OK;
+}
 
 }  // namespace
 
-extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
-                                             int32_t head_dim, int32_t max_context_len,
+extern "C" size_t pkv_decode_workspace_bytes(const pkv_cache_desc* c, int32_t num_seqs,
+                                             int32_t num_q_heads, int32_t max_context_len,
                                              int32_t partition_size) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
-  return workspace_for(num_seqs, num_q_heads, head_dim,
-                       parts_for(max_context_len, partition_size));
+  pkv__clear_error();
+  if (check_sizes(c, num_seqs, num_q_heads, max_context_len, partition_size) || num_seqs == 0)
+    return 0;
+  Plan pl;
+  if (make_plan(c, num_seqs, num_q_heads, max_context_len, partition_size, &pl)) return 0;
+  return pl.bytes;
 }
 
 extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
@@ -720,21 +1168,11 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
                                           float scale, int32_t partition_size, void* workspace,
                                           size_t workspace_bytes, void* stream) {
   pkv__clear_error();
-  int rc = pkv__check_desc(c);
+  int rc = check_sizes(c, num_seqs, num_q_heads, max_context_len, partition_size);
   if (rc) return rc;
-  if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || max_blocks_per_seq < 0)
-    return pkv__fail(PKV_EINVAL, "bad sizes (num_seqs=%d num_q_heads=%d max_context_len=%d width=%d)",
-                     num_seqs, num_q_heads, max_context_len, max_blocks_per_seq);
-  if (num_q_heads % c->num_kv_heads != 0)
-    return pkv__fail(PKV_EINVAL, "num_q_heads %d is not a multiple of num_kv_heads %d",
-                     num_q_heads, c->num_kv_heads);
-  const int32_t B = c->block_size;
-  if ((int64_t)max_blocks_per_seq * B < max_context_len)
+  if (max_blocks_per_seq < 0 || (int64_t)max_blocks_per_seq * c->block_size < max_context_len)
     return pkv__fail(PKV_EINVAL, "table width %d * block_size %d < max_context_len %d",
-                     max_blocks_per_seq, B, max_context_len);
-  if (partition_size < 0 || (partition_size > 0 && partition_size % B != 0))
-    return pkv__fail(PKV_EINVAL, "partition_size %d must be 0 or a positive multiple of block_size %d",
-                     partition_size, B);
+                     max_blocks_per_seq, c->block_size, max_context_len);
   if (!(scale == scale) || isinf(scale)) return pkv__fail(PKV_EINVAL, "scale is not finite");
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
@@ -743,15 +1181,14 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
       ((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u))
     return pkv__fail(PKV_EINVAL, "q, out and caches must be 16-byte aligned");
 
-  const int32_t parts = parts_for(max_context_len, partition_size);
-  // With no split, one partition holds the longest context.
-  const int32_t ps = parts == 1 ? (max_context_len > 0 ? ((max_context_len + B - 1) / B) * B : B)
-                                : partition_size;
-  const size_t need = workspace_for(num_seqs, num_q_heads, c->head_dim, parts);
-  if (workspace_bytes < need || (need && !workspace))
+  Plan pl;
+  rc = make_plan(c, num_seqs, num_q_heads, max_context_len, partition_size, &pl);
+  if (rc) return rc;
+  if (workspace_bytes < pl.bytes || (pl.bytes && !workspace))
     return pkv__fail(PKV_EINVAL, "workspace of %zu bytes is smaller than the %zu needed",
-                     workspace_bytes, need);
-  if (need && !aligned16(workspace)) return pkv__fail(PKV_EINVAL, "workspace must be 16-byte aligned");
+                     workspace_bytes, pl.bytes);
+  if (pl.bytes && !aligned16(workspace))
+    return pkv__fail(PKV_EINVAL, "workspace must be 16-byte aligned");
 
   LaunchArgs a;
   a.out = out;
@@ -766,13 +1203,14 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
   a.num_blocks = c->num_blocks;
   a.max_context_len = max_context_len;
   a.num_q_heads = num_q_heads;
-  a.num_parts = parts;
-  a.ps = ps;
+  a.plan = pl;
   a.qscale = scale * kLog2e;
-  a.part_ml = need ? (float*)workspace : nullptr;
-  a.part_o = need ? (float*)workspace + (size_t)num_seqs * num_q_heads * parts * 2 : nullptr;
+  char* ws = (char*)workspace;
+  a.meta = pl.bytes ? (int2*)(ws + pl.meta_off) : nullptr;
+  a.part_ml = pl.bytes ? (float*)(ws + pl.ml_off) : nullptr;
+  a.part_o = pl.bytes ? (float*)(ws + pl.o_off) : nullptr;
   a.stream = (hipStream_t)stream;
   const int G = num_q_heads / c->num_kv_heads;
-  if (c->dtype == PKV_BF16) return dispatch_d<BF16>(a, c->head_dim, B, G);
-  return dispatch_d<F32>(a, c->head_dim, B, G);
+  if (c->dtype == PKV_BF16) return dispatch_d<BF16>(a, c->head_dim, c->block_size, G);
+  return dispatch_d<F32>(a, c->head_dim, c->block_size, G);
 }

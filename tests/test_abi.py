@@ -17,10 +17,20 @@ def test_every_declared_symbol_is_exported():
 
 def test_workspace_bytes():
     # 64 seqs x 32 heads, ctx <= 4096 in 512-token partitions -> 8 partials of (2 + D) floats
-    assert pkv.decode_workspace_bytes(64, 32, 128, 4096, 512) == 64 * 32 * 8 * 130 * 4
-    assert pkv.decode_workspace_bytes(64, 32, 128, 512, 512) == 0     # one partition
-    assert pkv.decode_workspace_bytes(64, 32, 128, 4096, 0) == 0      # no split
-    assert pkv.decode_workspace_bytes(8, 32, 128, 32768, 512) == 8 * 32 * 64 * 130 * 4
+    d = pkv.CacheDesc(1000, 8, 16, 128, pkv.PKV_BF16)
+    assert pkv.decode_workspace_bytes(d, 64, 32, 4096, 512) == 64 * 32 * 8 * 130 * 4
+    assert pkv.decode_workspace_bytes(d, 64, 32, 512, 512) == 0     # one partition
+    assert pkv.decode_workspace_bytes(d, 64, 32, 4096, 0) == 0      # no split
+    assert pkv.decode_workspace_bytes(d, 8, 32, 32768, 512) == 8 * 32 * 64 * 130 * 4
+    assert pkv.decode_workspace_bytes(d, 0, 32, 32768, 512) == 0
+    # fp32 caches: the automatic split is 512-token partitions (no device query)
+    f = pkv.CacheDesc(1000, 8, 16, 128, pkv.PKV_F32)
+    assert pkv.decode_workspace_bytes(f, 64, 32, 4096, pkv.PKV_PARTITION_AUTO) == 64 * 32 * 8 * 130 * 4
+    for bad in ((d, 64, 32, 4096, 24), (d, 64, 30, 4096, 512), (d, -1, 32, 4096, 512),
+                (d, 64, 32, 4096, -2)):
+        with pytest.raises(pkv.PagedKVError) as e:
+            pkv.decode_workspace_bytes(*bad)
+        assert e.value.code == pkv.PKV_EINVAL
 
 
 def test_validate_write():

@@ -3,7 +3,8 @@
 Inputs are seeded (datagen); block tables come from the oracle's allocator;
 slots no sequence reads are poisoned with NaN.  Small cases compare every
 output element; the full-size workloads compare sampled sequences (all their
-heads) in the same launch configuration the benchmark times."""
+heads) in the same launch configuration the benchmark times (the balanced
+split, PKV_PARTITION_AUTO) and in split-context partitions."""
 
 import math
 import zlib
@@ -64,6 +65,8 @@ def _small_case(dtype, D, B, G, seed, hkv=2, lens=None):
     return q, kc, vc, tables, ctx, 1.0 / math.sqrt(D)
 
 
+AUTO = pkv.PKV_PARTITION_AUTO
+
 INSTANCES = [(dt, D, B, G) for dt in ("bf16", "f32") for D in (64, 128) for B in (8, 16, 32)
              for G in (1, 2, 4, 8)]
 
@@ -74,7 +77,7 @@ def test_every_instance_all_elements(inst):
     print(f"instance {inst}", flush=True)
     q, kc, vc, tables, ctx, scale = _small_case(dtype, D, B, G, zlib.crc32(repr(inst).encode()))
     ref = paged_attention_decode(q, kc, vc, tables, ctx, scale, dtype)
-    for ps in (0, 4 * B, 512):
+    for ps in (AUTO, 0, 4 * B, 512):
         out = _run_gpu(q, kc, vc, tables, ctx, scale, ps)
         check_close(out, ref, dtype)
         assert np.all(out[0] == 0), "an empty context gives zeros"
@@ -86,8 +89,9 @@ def test_workload_tiny_all_elements():
     tables, ctx = _tables(w.context_lens, w.num_blocks, sh.block_size, w.free_order)
     poison_unused(w.k_cache, w.v_cache, tables, ctx, sh.block_size, sh.dtype)
     ref = paged_attention_decode(w.q, w.k_cache, w.v_cache, tables, ctx, sh.scale, sh.dtype)
-    out = _run_gpu(w.q, w.k_cache, w.v_cache, tables, ctx, sh.scale, sh.partition_size)
-    print("tiny max_abs/max_rel", check_close(out, ref, sh.dtype))
+    for ps in (AUTO, sh.partition_size):
+        out = _run_gpu(w.q, w.k_cache, w.v_cache, tables, ctx, sh.scale, ps)
+        print("tiny max_abs/max_rel", ps, check_close(out, ref, sh.dtype))
 
 
 def _sample(ctx, rng, k):
@@ -97,13 +101,15 @@ def _sample(ctx, rng, k):
 
 
 @pytest.mark.parametrize("workload", [2, 4])
-def test_full_size_workload_sampled(workload):
+@pytest.mark.parametrize("split", ["auto", "partitions"])
+def test_full_size_workload_sampled(workload, split):
     w = datagen.decode_inputs(workload)
     sh = w.shape
     print(f"workload {workload}: S={sh.num_seqs} NB={w.num_blocks} ctx sum={int(w.context_lens.sum())}",
           flush=True)
     tables, ctx = _tables(w.context_lens, w.num_blocks, sh.block_size, w.free_order)
-    out = _run_gpu(w.q, w.k_cache, w.v_cache, tables, ctx, sh.scale, sh.partition_size)
+    ps = AUTO if split == "auto" else sh.partition_size
+    out = _run_gpu(w.q, w.k_cache, w.v_cache, tables, ctx, sh.scale, ps)
     rng = np.random.default_rng(77)
     seqs = _sample(ctx, rng, 6 if workload == 2 else 1)
     heads = list(range(sh.num_q_heads)) if workload == 2 else [0, 5, 17, 31]
@@ -123,16 +129,17 @@ def test_physical_permutation_bit_identical():
     kc2[perm] = kc
     vc2[perm] = vc
     t2 = perm[tables].astype(np.int32)
-    for ps in (0, 64):
+    for ps in (AUTO, 0, 64):
         a = _run_gpu(q, kc, vc, tables, ctx, scale, ps)
         b = _run_gpu(q, kc2, vc2, t2, ctx, scale, ps)
         assert np.array_equal(a, b)
 
 
-def test_deterministic_and_poison_blind():
+@pytest.mark.parametrize("ps", [AUTO, 128])
+def test_deterministic_and_poison_blind(ps):
     q, kc, vc, tables, ctx, scale = _small_case("bf16", 128, 16, 8, 9)
-    a = _run_gpu(q, kc, vc, tables, ctx, scale, 128)
-    b = _run_gpu(q, kc, vc, tables, ctx, scale, 128)
+    a = _run_gpu(q, kc, vc, tables, ctx, scale, ps)
+    b = _run_gpu(q, kc, vc, tables, ctx, scale, ps)
     assert np.array_equal(a, b)
     # replace every unread slot's NaN with ordinary numbers: same bits out
     rng = np.random.default_rng(10)
@@ -142,13 +149,14 @@ def test_deterministic_and_poison_blind():
     nan_v = ((vc_clean.astype(np.uint32) << 16).view(np.float32) != (vc_clean.astype(np.uint32) << 16).view(np.float32))
     vc_clean[nan_v] = normal(rng, (int(nan_v.sum()),), "bf16")
     assert nan_k.sum() > 0
-    c = _run_gpu(q, kc_clean, vc_clean, tables, ctx, scale, 128)
+    c = _run_gpu(q, kc_clean, vc_clean, tables, ctx, scale, ps)
     assert np.array_equal(a, c)
 
 
-def test_single_token_returns_value_bits():
+@pytest.mark.parametrize("ps", [AUTO, 0])
+def test_single_token_returns_value_bits(ps):
     q, kc, vc, tables, ctx, scale = _small_case("bf16", 128, 16, 4, 11, lens=[1, 1, 1])
-    out = _run_gpu(q, kc, vc, tables, ctx, scale, 0)
+    out = _run_gpu(q, kc, vc, tables, ctx, scale, ps)
     for s in range(3):
         for h in range(8):
             assert np.array_equal(out[s, h], vc[tables[s, 0], h // 4, 0])
@@ -159,7 +167,7 @@ def test_partition_sizes_agree():
                                                 lens=[1, 100, 1000, 3000, 4096, 2049])
     ref = paged_attention_decode(q, kc, vc, tables, ctx, scale, "bf16")
     outs = {}
-    for ps in (0, 16, 64, 256, 512, 1024, 4096):
+    for ps in (AUTO, 0, 16, 64, 256, 512, 1024, 4096):
         outs[ps] = _run_gpu(q, kc, vc, tables, ctx, scale, ps)
         check_close(outs[ps], ref, "bf16")
 
@@ -184,3 +192,52 @@ def test_rejects_bad_arguments_without_launch():
     assert e.value.code == pkv.PKV_EUNSUPPORTED
     torch.cuda.synchronize()
     assert torch.count_nonzero(out) == 0
+
+
+kTILE = 16
+
+
+def _num_workers():
+    return torch.cuda.get_device_properties(0).multi_processor_count * 4 * 2
+
+
+def test_balanced_workspace_bytes():
+    d = pkv.CacheDesc(1000, 8, 16, 128, pkv.PKV_BF16)
+    pairs, nw, G = 64 * 8, _num_workers(), 4
+    slots = (pairs + nw) * G
+    a256 = lambda x: (x + 255) // 256 * 256
+    assert pkv.decode_workspace_bytes(d, 64, 32, 4096, AUTO) == a256(pairs * 8) + a256(slots * 8) + slots * 128 * 4
+    # too many sequences for the balanced split: 512-token partitions instead
+    assert pkv.decode_workspace_bytes(d, 8192, 32, 4096, AUTO) == 8192 * 32 * 8 * 130 * 4
+
+
+@pytest.mark.parametrize("case", ["many_short_pairs", "one_long_pair", "above_balanced_limit"])
+def test_balanced_split_edge_cases(case):
+    """Workers whose share spans many pairs (with empty sequences between them),
+    a pair shared by every worker, and the fallback past the balanced limit."""
+    print(f"case {case}", flush=True)
+    rng = np.random.default_rng(zlib.crc32(case.encode()))
+    if case == "many_short_pairs":
+        S, hkv, G, D, B = 3000, 2, 4, 128, 16
+        lens = rng.integers(0, 41, size=S)
+        lens[rng.random(S) < 0.1] = 0
+    elif case == "one_long_pair":
+        S, hkv, G, D, B = 1, 1, 8, 128, 16
+        lens = np.array([_num_workers() * kTILE + 7])
+    else:
+        S, hkv, G, D, B = 8192, 1, 2, 64, 8
+        lens = rng.integers(1, 25, size=S)
+    ctx = np.array(lens, np.int32)
+    need = int(sum(-(-int(n) // B) for n in ctx))
+    nb = need + 5
+    order = rng.permutation(nb).astype(np.int32)
+    q = normal(rng, (S, hkv * G, D), "bf16")
+    kc = normal(rng, (nb, hkv, B, D), "bf16")
+    vc = normal(rng, (nb, hkv, B, D), "bf16")
+    tables, ctx = _tables(ctx, nb, B, order)
+    poison_unused(kc, vc, tables, ctx, B, "bf16")
+    out = _run_gpu(q, kc, vc, tables, ctx, 1.0 / math.sqrt(D), AUTO)
+    seqs = list(range(S)) if S <= 3000 else sorted(set(rng.choice(S, 200, replace=False).tolist()) | {0, S - 1})
+    ref = paged_attention_decode(q, kc, vc, tables, ctx, 1.0 / math.sqrt(D), "bf16", seqs=seqs)
+    print("max_abs/max_rel", check_close(out[seqs], ref[seqs], "bf16"))
+    assert np.all(out[ctx == 0] == 0)
