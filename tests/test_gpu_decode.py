@@ -241,3 +241,30 @@ def test_balanced_split_edge_cases(case):
     ref = paged_attention_decode(q, kc, vc, tables, ctx, 1.0 / math.sqrt(D), "bf16", seqs=seqs)
     print("max_abs/max_rel", check_close(out[seqs], ref[seqs], "bf16"))
     assert np.all(out[ctx == 0] == 0)
+
+
+def test_balanced_workspace_reused_across_calls():
+    """One workspace serves consecutive calls with different context lengths:
+    whatever an earlier call left in it never reaches a later result."""
+    S, hkv, G, D, B = 40, 2, 4, 128, 16
+    d = pkv.CacheDesc(1, hkv, B, D, pkv.PKV_BF16)
+    max_ctx = 3000
+    need = pkv.decode_workspace_bytes(d, S, hkv * G, max_ctx, AUTO)
+    ws = torch.full((need,), 0x5A, dtype=torch.uint8, device="cuda")  # stale bytes
+    for rep in range(3):
+        rng = np.random.default_rng(100 + rep)
+        lens = rng.integers(0, max_ctx + 1, size=S)
+        ctx = np.array(lens, np.int32)
+        nb = int(sum(-(-int(n) // B) for n in ctx)) + 3
+        q = normal(rng, (S, hkv * G, D), "bf16")
+        kc = normal(rng, (nb, hkv, B, D), "bf16")
+        vc = normal(rng, (nb, hkv, B, D), "bf16")
+        tables, ctx = _tables(ctx, nb, B, rng.permutation(nb).astype(np.int32))
+        poison_unused(kc, vc, tables, ctx, B, "bf16")
+        dq = dev(q)
+        out = torch.empty_like(dq)
+        pkv.paged_attention_decode(out, dq, dev(kc), dev(vc), dev(tables), dev(ctx),
+                                   1.0 / math.sqrt(D), int(ctx.max()), AUTO, workspace=ws)
+        torch.cuda.synchronize()
+        ref = paged_attention_decode(q, kc, vc, tables, ctx, 1.0 / math.sqrt(D), "bf16")
+        print("rep", rep, check_close(host(out), ref, "bf16"))
