@@ -661,8 +661,10 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_kernel(
 // A worker's share cuts the pair list into segments; for each segment the
 // worker either writes the finished output (it holds the whole pair) or a
 // partial (m, l, o) to slot (pair + w), and the worker holding a pair's first
-// tile records which workers cover the pair.  Slots are distinct: along the
-// tile list, pair + worker grows by at least one at every segment start.
+// tile records which workers cover the pair (every pair's record is rewritten
+// on every call: empty sequences' pairs are marked by the workgroups).  Slots
+// are distinct: along the tile list, pair + worker grows by at least one at
+// every segment start.
 
 // Number of the worker whose share [w T / nw, (w + 1) T / nw) holds tile u.
 __device__ inline int worker_of(int64_t u, int64_t total, int32_t num_workers) {
@@ -718,6 +720,14 @@ __global__ __launch_bounds__(kThreads) void decode_balanced_kernel(
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int hq = num_kv_heads * G;
+  // No worker covers an empty sequence: its outputs are zeros here, and its
+  // pairs are marked so that the combine kernel skips them.
+  for (int i = blockIdx.x; i < num_seqs; i += gridDim.x) {
+    if (sm_n[i] != 0) continue;
+    for (int e = threadIdx.x; e < hq * D; e += kThreads) out[(int64_t)i * hq * D + e] = 0;
+    for (int g = threadIdx.x; g < num_kv_heads; g += kThreads)
+      meta[(int64_t)i * num_kv_heads + g] = make_int2(-1, -1);
+  }
   const int64_t total = (int64_t)num_kv_heads * sm_c[num_seqs];
   // With fewer tiles than workers only the first `total` workers take one
   // each: every worker in [0, nw) has a non-empty share, so the workers that
@@ -764,13 +774,21 @@ __global__ __launch_bounds__(kThreads) void decode_balanced_kernel(
   };
   // Block-table entry of this lane's row of tile x (a valid entry of the
   // sequence's row even for rows past its end).
+  // The tile of the pair processed at place x.tile.  Pair (s, g)'s order is
+  // rotated by g nt / Hkv tiles, so the workers on the KV heads of one
+  // sequence, which move through their pairs side by side, do not read the
+  // head runs of the same physical blocks at the same moment.
+  auto ptile = [&](const Pos& x) {
+    const int r = x.tile + (x.g * x.nt) / num_kv_heads;
+    return r >= x.nt ? r - x.nt : r;
+  };
   auto table_entry = [&](const Pos& x) {
-    const int t = min(x.tile * kTile + col, x.n - 1);
+    const int t = min(ptile(x) * kTile + col, x.n - 1);
     return block_tables[(int64_t)x.s * table_width + t / B];
   };
   const uint16_t* safe = q + 8 * grp;
   auto load_tile = [&](const Pos& x, int phys, bool live, KVTile<D>& kv) {
-    const int t = x.tile * kTile + col;
+    const int t = ptile(x) * kTile + col;
     load_kv<D, B>(kv, k_cache, v_cache, safe, live && t < x.n, phys, t, x.g, num_kv_heads,
                   num_blocks, grp);
   };
@@ -782,7 +800,7 @@ __global__ __launch_bounds__(kThreads) void decode_balanced_kernel(
   // Update with tile u (place x); at the end of a segment write its result
   // and prepare for the next pair (place nx).
   auto step = [&](const Pos& x, int64_t u, KVTile<D>& kv, const Pos& nx) {
-    at.update(kv, min(kTile, x.n - x.tile * kTile), qscale, grp);
+    at.update(kv, min(kTile, x.n - ptile(x) * kTile), qscale, grp);
     if (x.tile + 1 < x.nt && u + 1 < u1) return;
     const int64_t pair_u0 = (int64_t)num_kv_heads * sm_c[x.s] + (int64_t)x.g * x.nt;
     const int pair = x.s * num_kv_heads + x.g;
@@ -872,76 +890,63 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(
 
 // One wave per (pair, query head) of the balanced split: pairs covered by
 // several workers are combined here, in worker order,
-// out = sum_w o_w 2^(m_w - m*) / sum_w L_w 2^(m_w - m*); heads of empty
-// sequences get zeros; pairs finished by a single worker are left alone.
-// The lanes first fold the workers' (m, L) in parallel (fixed butterfly
-// order), then walk the workers' output rows with D / 64 dims per lane.
+// out = sum_w o_w 2^(m_w - m*) / sum_w L_w 2^(m_w - m*).  Pairs finished by a
+// single worker, and pairs of empty sequences, are left alone.  Every lane
+// fetches up to kChunk workers' (m, L) and its D / 64 output dims with
+// independent loads and folds them into a running (max, sum, output).
+// Four such waves share a workgroup: dispatching one-wave workgroups costs
+// about as much as the whole combine.
 template <int D, int G>
-__global__ __launch_bounds__(kWave) void decode_balanced_reduce_kernel(
+__global__ __launch_bounds__(kThreads) void decode_balanced_reduce_kernel(
     uint16_t* __restrict__ out, const int2* __restrict__ meta, const float* __restrict__ part_ml,
-    const float* __restrict__ part_o, const int32_t* __restrict__ context_lens,
-    int32_t num_kv_heads, int32_t max_context_len, int32_t num_workers) {
+    const float* __restrict__ part_o, int32_t num_pairs, int32_t num_workers) {
   constexpr int DPL = D / kWave;  // dims per lane
-  constexpr int kUnroll = 8;
+  constexpr int kChunk = 16;
   static_assert(DPL * kWave == D, "head_dim must be a multiple of 64");
-  const int pair = blockIdx.x / G;
-  const int h = blockIdx.x - pair * G;
-  const int lane = threadIdx.x;
-  const int s = pair / num_kv_heads;
-  uint16_t* orow = out + ((int64_t)pair * G + h) * D + lane * DPL;
-  const int n = min(max(context_lens[s], 0), max_context_len);
-  if (n == 0) {
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) store_out(orow + e, 0.0f);
-    return;
-  }
+  const int unit = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  if (unit >= num_pairs * G) return;
+  const int pair = unit / G;
+  const int h = unit - pair * G;
+  const int lane = threadIdx.x & (kWave - 1);
   const int2 mt = meta[pair];
   const int wa = max(mt.x, 0), wb = min(mt.y, num_workers - 1);
-  if (wa >= wb) return;
+  if (mt.x < 0 || wa >= wb) return;
   const int nseg = wb - wa + 1;
   const float* ml = part_ml + (((int64_t)pair + wa) * G + h) * 2;  // worker k at ml[k * 2 G]
   const float* po = part_o + (((int64_t)pair + wa) * G + h) * D + lane * DPL;
-
-  // (max, sum) over this lane's workers k = lane, lane + 64, ...
-  float M = -INFINITY, L = 0.0f;
-  for (int k = lane; k < nseg; k += kWave) {
-    const float2 v = *reinterpret_cast<const float2*>(ml + (int64_t)k * 2 * G);
-    const float mx = fmaxf(M, v.x);
-    L = L * (M == -INFINITY ? 0.0f : exp2f(M - mx)) + v.y * exp2f(v.x - mx);
-    M = mx;
-  }
-  // butterfly over the wave: every lane ends with the same bits
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const float om = __shfl_xor(M, off, kWave);
-    const float ol = __shfl_xor(L, off, kWave);
-    const float mx = fmaxf(M, om);
-    const float a = M == -INFINITY ? 0.0f : L * exp2f(M - mx);
-    const float b = om == -INFINITY ? 0.0f : ol * exp2f(om - mx);
-    L = (lane & off) ? b + a : a + b;
-    M = mx;
-  }
-  float O[DPL];
+  float M = -INFINITY, L = 0.0f, O[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) O[e] = 0.0f;
-  for (int k0 = 0; k0 < nseg; k0 += kUnroll) {
-    float mv[kUnroll], ov[kUnroll][DPL];
+  for (int k0 = 0; k0 < nseg; k0 += kChunk) {
+    float2 mlv[kChunk];
+    float ov[kChunk][DPL];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int k = min(k0 + u, nseg - 1);
-      mv[u] = ml[(int64_t)k * 2 * G];
+    for (int c = 0; c < kChunk; ++c) {
+      const int64_t k = min(k0 + c, nseg - 1);
+      mlv[c] = *reinterpret_cast<const float2*>(ml + k * 2 * G);
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) ov[u][e] = po[(int64_t)k * G * D + e];
+      for (int e = 0; e < DPL; ++e) ov[c][e] = po[k * G * D + e];
     }
+    float cm = M;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if (k0 + u < nseg) {
-        const float f = exp2f(mv[u] - M);
+    for (int c = 0; c < kChunk; ++c)
+      if (k0 + c < nseg) cm = fmaxf(cm, mlv[c].x);
+    const float a = M == -INFINITY ? 0.0f : exp2f(M - cm);
+    L *= a;
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) O[e] = fmaf(ov[u][e], f, O[e]);
+    for (int e = 0; e < DPL; ++e) O[e] *= a;
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+      if (k0 + c < nseg) {
+        const float f = exp2f(mlv[c].x - cm);
+        L = fmaf(mlv[c].y, f, L);
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) O[e] = fmaf(ov[c][e], f, O[e]);
       }
     }
+    M = cm;
   }
+  uint16_t* orow = out + ((int64_t)pair * G + h) * D + lane * DPL;
 #pragma unroll
   for (int e = 0; e < DPL; ++e) store_out(orow + e, O[e] / L);
 }
@@ -1060,11 +1065,11 @@ int launch(const LaunchArgs& a) {
                          a.plan.workers, a.qscale);
       int rc = check_launch("decode_balanced");
       if (rc) return rc;
+      const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * G;
       hipLaunchKernelGGL((decode_balanced_reduce_kernel<D, G>),
-                         dim3((uint32_t)(a.num_seqs * a.num_kv_heads * G)), dim3(kWave), 0, a.stream,
-                         (uint16_t*)a.out, (const int2*)a.meta, (const float*)a.part_ml,
-                         (const float*)a.part_o, a.context_lens, a.num_kv_heads, a.max_context_len,
-                         a.plan.workers);
+                         dim3((uint32_t)((units + kWaves - 1) / kWaves)), dim3(kThreads), 0,
+                         a.stream, (uint16_t*)a.out, (const int2*)a.meta, (const float*)a.part_ml,
+                         (const float*)a.part_o, a.num_seqs * a.num_kv_heads, a.plan.workers);
       return check_launch("decode_balanced_reduce");
     }
   }
