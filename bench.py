@@ -12,6 +12,9 @@ uploaded, so the timed region starts with every input resident in HBM.
 Workloads (seeded synthetic inputs, see datagen):
   2  64 seqs, 32 q / 8 kv heads, head_dim 128, bf16, block 16,
      context U{128..4096}  (default; the headline configuration)
+  3  16 prompts of 2048 - U{1..15} tokens x 8 samples sharing the prompt
+     blocks, after U{1..256} generated tokens each; copy_blocks of the first
+     generation step's 112 copy-on-write pairs is timed on its own
   4  8 seqs x 32768 tokens, same heads
   5  256 seqs, context log-uniform 16..8192, 64 q / 8 kv heads (--block-size)
 
@@ -36,6 +39,8 @@ HBM_PEAK_GBPS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 WORKLOAD_NAMES = {
+    3: "parallel-sampling decode: 16 prompts of 2048 - U{1..15} tokens x 8 samples sharing the "
+       "prompt blocks, U{1..256} generated tokens each, 32 q / 8 kv heads, head_dim 128, bf16, block 16",
     2: "llama3-8b-layer decode: 64 seqs, 32 q / 8 kv heads, head_dim 128, bf16, block 16, "
        "context U{128..4096}, pool 1.25x need, blocks scattered",
     4: "long-context decode: 8 seqs x 32768 tokens, 32 q / 8 kv heads, head_dim 128, bf16, "
@@ -50,7 +55,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, choices=[2, 4, 5])
+    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5])
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--partition-size", type=int, default=-1,
                     help="-1: balanced split (default); > 0: split-context partitions; 0: no split")
@@ -71,6 +76,10 @@ class Workload:
         import paged_kv_cache_377_amd as pkv
 
         self.workload = workload
+        self.copy_pairs = None
+        if workload == 3:
+            self._init_sampling(steps_total, seed_extra)
+            return
         if workload == 5:
             w = datagen.mixed_step_inputs(block_size or 16)
             # the cache holds ctx - 1 tokens; the first step appends the last one
@@ -117,6 +126,65 @@ class Workload:
                 nv = datagen.normal(rng, (S, sh.num_kv_heads, sh.head_dim), sh.dtype)
             q = w.q if i == 0 else datagen.normal(rng, w.q.shape, sh.dtype)
             self.steps.append(dict(slots=slots, pairs=pairs, tables=tables, ctx=ctx, k=nk, v=nv, q=q))
+
+    def _init_sampling(self, steps_total: int, seed_extra: int):
+        """Run the whole sampling trace through the library's allocator; the
+        pool holds N(0,1) values (the decode's cost does not depend on them)."""
+        import datagen
+        import paged_kv_cache_377_amd as pkv
+
+        plan = datagen.sampling_plan()
+        sh = plan.shape
+        B, S = sh.block_size, sh.num_seqs
+        grow = -(-steps_total // B) + 1
+        nb = plan.num_blocks + S * grow
+        rng = np.random.default_rng(datagen.seed_for(3) + 17)
+        order = np.concatenate([plan.free_order, plan.num_blocks +
+                                rng.permutation(nb - plan.num_blocks)]).astype(np.int32)
+        self.alloc = pkv.BlockAllocator(nb, B, order)
+        for op in datagen.sampling_ops(plan):
+            if op[0] == "add":
+                self.alloc.add(op[1], op[2])
+            elif op[0] == "fork":
+                self.alloc.fork(op[1], op[2])
+            else:
+                _, pairs = self.alloc.step(op[1])
+                if self.copy_pairs is None:
+                    self.copy_pairs = pairs
+        pool = (nb, sh.num_kv_heads, B, sh.head_dim)
+        q = datagen.normal(rng, (S, sh.num_q_heads, sh.head_dim), sh.dtype)
+        kc = datagen.normal(rng, pool, sh.dtype)
+        vc = datagen.normal(rng, pool, sh.dtype)
+        self.seq_ids = np.arange(S, dtype=np.int64)
+        lens = [self.alloc.info(int(x))[0] for x in self.seq_ids]
+        self.w = datagen.DecodeInputs(3, sh, np.array(lens, np.int32), nb, order, q, kc, vc)
+        self.shape = sh
+        self.num_blocks = nb
+        self.width = -(-(max(lens) + steps_total) // B)
+        rng = np.random.default_rng(datagen.seed_for(3) + 31 + seed_extra)
+        self.steps = []
+        for i in range(steps_total):
+            slots, pairs = self.alloc.step(self.seq_ids)
+            tables, ctx = self.alloc.build_tables(self.seq_ids, self.width)
+            nk = datagen.normal(rng, (S, sh.num_kv_heads, sh.head_dim), sh.dtype)
+            nv = datagen.normal(rng, (S, sh.num_kv_heads, sh.head_dim), sh.dtype)
+            qi = q if i == 0 else datagen.normal(rng, q.shape, sh.dtype)
+            self.steps.append(dict(slots=slots, pairs=pairs, tables=tables, ctx=ctx, k=nk, v=nv, q=qi))
+
+    def unique_kv_bytes(self, i: int) -> int:
+        """K/V bytes of the distinct (block, row) slots the decode reads."""
+        sh = self.shape
+        st = self.steps[i]
+        B = sh.block_size
+        seen = set()
+        for row, n in zip(st["tables"], st["ctx"]):
+            for b in range(-(-int(n) // B)):
+                rows = min(B, int(n) - b * B)
+                seen.add((int(row[b]), rows))
+        by_block = {}
+        for blk, rows in seen:
+            by_block[blk] = max(by_block.get(blk, 0), rows)
+        return sum(by_block.values()) * sh.num_kv_heads * sh.head_dim * 2 * sh.elem_bytes
 
     def kv_bytes(self, i: int) -> int:
         sh = self.shape
@@ -301,6 +369,24 @@ def main():
     torch.cuda.synchronize()
     dec_avg_ms = ev2.elapsed_time(ev3) / args.steps
 
+    copy_rec = None
+    if wl.copy_pairs is not None and len(wl.copy_pairs):
+        # copy_blocks of the first generation step's pairs, replayed (idempotent)
+        dpairs = to_dev(wl.copy_pairs, torch)
+        kc, vc = kcs[0], vcs[0]
+        pkv.copy_blocks(kc, vc, dpairs, stream=stream)
+        ev4, ev5 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev4.record(stream)
+        for _ in range(args.steps):
+            pkv.copy_blocks(kc, vc, dpairs, stream=stream)
+        ev5.record(stream)
+        torch.cuda.synchronize()
+        cus = ev4.elapsed_time(ev5) * 1e3 / args.steps
+        moved = 2 * len(wl.copy_pairs) * 2 * sh.num_kv_heads * sh.block_size * sh.head_dim * sh.elem_bytes
+        copy_rec = {"pairs": int(len(wl.copy_pairs)), "us": round(cus, 2),
+                    "bytes_read_plus_written": moved, "gbps": round(moved / cus / 1e3, 1)}
+
     timed = range(args.warmup, total)
     kv = sum(wl.kv_bytes(i) for i in timed)
     alg = sum(wl.algorithmic_bytes(i) for i in timed)
@@ -339,9 +425,15 @@ def main():
                      "algorithmic_bytes_per_launch": int(alg / args.steps)},
         "allocator_us_per_step": None,
     }
+    if args.workload == 3:
+        uniq = wl.unique_kv_bytes(args.warmup)
+        res["unique_kv_gbps"] = round(uniq / (dec_avg_ms * 1e-3) / 1e9, 1)
+        res["logical_kv_gbps"] = round(wl.kv_bytes(args.warmup) / (dec_avg_ms * 1e-3) / 1e9, 1)
+        res["copy_blocks"] = copy_rec
     # host allocator cost per step (not in the timed GPU region)
     import paged_kv_cache_377_amd as pkv2
-    a2 = pkv2.BlockAllocator(wl.num_blocks, sh.block_size)
+    need = sum(-(-(int(n) + 50) // sh.block_size) for n in wl.steps[0]["ctx"]) + sh.num_seqs
+    a2 = pkv2.BlockAllocator(need, sh.block_size)
     for s in range(sh.num_seqs):
         a2.add(s, int(wl.steps[0]["ctx"][s]) - 1)
     t1 = time.perf_counter()

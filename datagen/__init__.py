@@ -247,3 +247,25 @@ def poison_unused(k_cache: np.ndarray, v_cache: np.ndarray, tables, context_lens
     vb = v_cache.transpose(0, 2, 1, 3)
     kb[dead] = nan
     vb[dead] = nan
+
+
+def sampling_ops(plan: SamplingPlan):
+    """The operation stream of workload 3, as plain tuples (no arithmetic of the
+    method: which sequence to admit, fork or step, in which order).
+
+      ("add", seq, n)          admit sample 0 of a prompt with its n prompt tokens
+      ("fork", parent, child)  samples 1 .. samples-1 start as copies of sample 0
+      ("step", [seqs])         one generation step of every still-generating
+                               sample, in increasing id order (round-robin)
+
+    Sequence id of sample j of prompt p is p * samples + j.
+    """
+    S = plan.samples
+    P = len(plan.prompt_lens)
+    for p in range(P):
+        yield ("add", p * S, int(plan.prompt_lens[p]))
+        for j in range(1, S):
+            yield ("fork", p * S, p * S + j)
+    for i in range(int(plan.gen_lens.max())):
+        active = [s for s in range(P * S) if int(plan.gen_lens[s]) > i]
+        yield ("step", active)
