@@ -17,6 +17,9 @@ Workloads (seeded synthetic inputs, see datagen):
      generation step's 112 copy-on-write pairs is timed on its own
   4  8 seqs x 32768 tokens, same heads
   5  256 seqs, context log-uniform 16..8192, 64 q / 8 kv heads (--block-size)
+  6  prefix caching: 64 requests = one 1024-token system prompt + their own
+     U{16..1024}-token question, admitted by token ids through the
+     allocator's prefix cache (host admission cost and hit rate reported)
 
 Prints one JSON line.  ``value`` = algorithmic KV bytes the decode reads per
 step / step time, in GB/s (1e9 B/s).  ``roofline`` reports the decode call
@@ -47,6 +50,8 @@ WORKLOAD_NAMES = {
        "block 16, partitions of 512",
     5: "mixed decode + append: 256 seqs, context log-uniform 16..8192, 64 q / 8 kv heads, "
        "head_dim 128, bf16",
+    6: "prefix-cached decode: 64 requests = shared 1024-token system prompt + U{16..1024}-token "
+       "question, 32 q / 8 kv heads, head_dim 128, bf16, block 16",
 }
 
 
@@ -55,7 +60,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6])
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--partition-size", type=int, default=-1,
                     help="-1: balanced split (default); > 0: split-context partitions; 0: no split")
@@ -77,8 +82,12 @@ class Workload:
 
         self.workload = workload
         self.copy_pairs = None
+        self.prefix_rec = None
         if workload == 3:
             self._init_sampling(steps_total, seed_extra)
+            return
+        if workload == 6:
+            self._init_prefix(steps_total, seed_extra)
             return
         if workload == 5:
             w = datagen.mixed_step_inputs(block_size or 16)
@@ -165,6 +174,57 @@ class Workload:
         self.steps = []
         for i in range(steps_total):
             slots, pairs = self.alloc.step(self.seq_ids)
+            tables, ctx = self.alloc.build_tables(self.seq_ids, self.width)
+            nk = datagen.normal(rng, (S, sh.num_kv_heads, sh.head_dim), sh.dtype)
+            nv = datagen.normal(rng, (S, sh.num_kv_heads, sh.head_dim), sh.dtype)
+            qi = q if i == 0 else datagen.normal(rng, q.shape, sh.dtype)
+            self.steps.append(dict(slots=slots, pairs=pairs, tables=tables, ctx=ctx, k=nk, v=nv, q=qi))
+
+    def _init_prefix(self, steps_total: int, seed_extra: int):
+        """Admit every request by its token ids through the library's prefix
+        cache (timed on the host); the pool holds N(0,1) values."""
+        import datagen
+        import paged_kv_cache_377_amd as pkv
+
+        probe = datagen.prefix_plan()
+        sh = probe.shape
+        B, S = sh.block_size, sh.num_seqs
+        plan = datagen.prefix_plan(spare_blocks=S * (-(-steps_total // B) + 1))
+        nb = plan.num_blocks
+        prompts = [plan.prompt(r) for r in range(S)]
+        self.alloc = pkv.BlockAllocator(nb, B, plan.free_order, prefix_caching=True)
+        cached = 0
+        t0 = time.perf_counter()
+        for r in range(S):
+            _, c = self.alloc.add_tokens(r, prompts[r])
+            cached += c
+        admit_s = time.perf_counter() - t0
+        st = self.alloc.cache_stats()
+        total = int(sum(len(p) for p in prompts))
+        self.prefix_rec = {
+            "requests": S, "prompt_tokens": total, "cached_tokens": int(cached),
+            "prefill_skipped_frac": round(cached / total, 4), "hit_rate": round(st["hit_rate"], 4),
+            "hits": int(st["hits"]), "queries": int(st["queries"]),
+            "admit_us_per_request": round(admit_s * 1e6 / S, 2),
+            "admit_ns_per_token": round(admit_s * 1e9 / total, 2),
+            "blocks_in_use": int(nb - self.alloc.stats()["num_free"]),
+            "blocks_without_sharing": int(sum(-(-len(p) // B) for p in prompts))}
+        rng = np.random.default_rng(datagen.seed_for(6) + 17)
+        pool = (nb, sh.num_kv_heads, B, sh.head_dim)
+        q = datagen.normal(rng, (S, sh.num_q_heads, sh.head_dim), sh.dtype)
+        kc = datagen.normal(rng, pool, sh.dtype)
+        vc = datagen.normal(rng, pool, sh.dtype)
+        self.seq_ids = np.arange(S, dtype=np.int64)
+        lens = [len(p) for p in prompts]
+        self.w = datagen.DecodeInputs(6, sh, np.array(lens, np.int32), nb, plan.free_order, q, kc, vc)
+        self.shape = sh
+        self.num_blocks = nb
+        self.width = -(-(max(lens) + steps_total) // B)
+        rng = np.random.default_rng(datagen.seed_for(6) + 31 + seed_extra)
+        self.steps = []
+        for i in range(steps_total):
+            ids = rng.integers(0, 32000, size=S).astype(np.int32)
+            slots, pairs = self.alloc.step(self.seq_ids, ids)
             tables, ctx = self.alloc.build_tables(self.seq_ids, self.width)
             nk = datagen.normal(rng, (S, sh.num_kv_heads, sh.head_dim), sh.dtype)
             nv = datagen.normal(rng, (S, sh.num_kv_heads, sh.head_dim), sh.dtype)
@@ -425,11 +485,14 @@ def main():
                      "algorithmic_bytes_per_launch": int(alg / args.steps)},
         "allocator_us_per_step": None,
     }
-    if args.workload == 3:
+    if args.workload in (3, 6):
         uniq = wl.unique_kv_bytes(args.warmup)
         res["unique_kv_gbps"] = round(uniq / (dec_avg_ms * 1e-3) / 1e9, 1)
         res["logical_kv_gbps"] = round(wl.kv_bytes(args.warmup) / (dec_avg_ms * 1e-3) / 1e9, 1)
-        res["copy_blocks"] = copy_rec
+        if args.workload == 3:
+            res["copy_blocks"] = copy_rec
+        else:
+            res["prefix_cache"] = wl.prefix_rec
     # host allocator cost per step (not in the timed GPU region)
     import paged_kv_cache_377_amd as pkv2
     need = sum(-(-(int(n) + 50) // sh.block_size) for n in wl.steps[0]["ctx"]) + sh.num_seqs

@@ -30,7 +30,7 @@ from __future__ import annotations
 
 import math
 from dataclasses import dataclass, field
-from typing import Optional
+from typing import List, Optional
 
 import numpy as np
 
@@ -97,6 +97,7 @@ SHAPES = {
     3: Shape(128, 32, 8, 128, 16, "bf16", 1.0 / math.sqrt(128), 512),
     4: Shape(8, 32, 8, 128, 16, "bf16", 1.0 / math.sqrt(128), 512),
     5: Shape(256, 64, 8, 128, 16, "bf16", 1.0 / math.sqrt(128), 512),
+    6: Shape(64, 32, 8, 128, 16, "bf16", 1.0 / math.sqrt(128), 512),
 }
 
 
@@ -269,3 +270,37 @@ def sampling_ops(plan: SamplingPlan):
     for i in range(int(plan.gen_lens.max())):
         active = [s for s in range(P * S) if int(plan.gen_lens[s]) > i]
         yield ("step", active)
+
+
+@dataclass
+class PrefixPlan:
+    """Prefix-cache workload: requests that open with one shared system prompt
+    (page 3, section 04: a repeated system prompt, then each user's own
+    question).  Token ids are labels drawn uniformly from a 32000-id vocabulary."""
+    shape: Shape
+    system: np.ndarray                # [system_len] int32
+    suffixes: List[np.ndarray]        # per request, [suffix_len] int32
+    num_blocks: int
+    free_order: np.ndarray
+
+    def prompt(self, r: int) -> np.ndarray:
+        return np.concatenate([self.system, self.suffixes[r]]).astype(np.int32)
+
+
+def prefix_plan(seed: Optional[int] = None, num_requests: int = 64, system_len: int = 1024,
+                suffix_min: int = 16, suffix_max: int = 1024, vocab: int = 32000,
+                spare_blocks: int = 0) -> PrefixPlan:
+    """64 requests = a 1024-token system prompt + a suffix of U{16..1024} tokens,
+    Llama-3-8B layer shape; the pool is 1.25x the blocks the prompts need with
+    sharing, plus ``spare_blocks``, in a seeded random order."""
+    sh = shape(6)
+    sh.num_seqs = num_requests
+    rng = np.random.default_rng(seed_for(6) if seed is None else seed)
+    system = rng.integers(0, vocab, size=system_len).astype(np.int32)
+    lens = rng.integers(suffix_min, suffix_max, size=num_requests, endpoint=True)
+    suffixes = [rng.integers(0, vocab, size=int(n)).astype(np.int32) for n in lens]
+    B = sh.block_size
+    need = -(-system_len // B) + sum(-(-int(n) // B) + 1 for n in lens)
+    nb = int(math.ceil(1.25 * need)) + spare_blocks
+    order = rng.permutation(nb).astype(np.int32)
+    return PrefixPlan(sh, system, suffixes, nb, order)

@@ -282,6 +282,69 @@ int pkv_alloc_stats(const pkv_alloc* a, pkv_stats* out);
 int pkv_alloc_export(const pkv_alloc* a, int32_t* free_fifo_out, int32_t* num_free_out,
                      int32_t* ref_cnt_out);
 
+/*
+ * Prefix caching (weishuz.com Month 2, section 04: a computed prompt's K/V
+ * stay in device memory and a later prompt with the same leading tokens maps
+ * the same blocks instead of computing them again; section 03 reading (2): a
+ * map from block hash to block beside the free list; section 07: hit-rate
+ * metric).
+ *
+ * Keys: full blocks only.  The key of logical block i is the chain hash
+ * h_i = H(h_{i-1}, ids of its B tokens), so it covers the whole prefix; a hit
+ * also compares the block's ids and h_{i-1}.  A full block is entered once the
+ * tokens that fill it have slots: prompt blocks by pkv_seq_add_tokens, later
+ * blocks by appends that carry token ids; under an existing key the first
+ * block entered stays.  A block whose count drops to 0 stays cached in the
+ * free list (release order); a hit takes it back out; the free list hands out
+ * its head and that block's entry is then evicted (least recently released
+ * first; a referenced block is never evicted).
+ */
+typedef struct {
+  int32_t enabled;
+  int32_t cached_blocks;     /* blocks currently in the map                     */
+  int64_t queries;           /* full prompt blocks looked up                    */
+  int64_t hits;              /* of those, found in the cache                    */
+  int64_t evictions;         /* cached blocks handed out again                  */
+  double hit_rate;           /* hits / queries (0 if none)                      */
+} pkv_prefix_stats;
+
+/* Turn prefix caching on.  Only before the first sequence is added
+ * (PKV_EINVAL otherwise); it stays on for the handle's life. */
+int pkv_prefix_cache_enable(pkv_alloc* a);
+
+/*
+ * Admit `seq` with its prompt's token ids tokens[0..num_tokens-1] (host).
+ * With prefix caching, the prompt's leading full blocks found in the cache
+ * are mapped (the walk stops at the first miss) and *num_cached_out (may be
+ * NULL) receives the number of leading positions whose K/V the pool already
+ * holds (a multiple of block_size): the caller writes K/V only for positions
+ * from there on.  The hits are taken back first, then fresh blocks from the
+ * free-list head, then the missed full blocks are entered.  slots_out: host
+ * [num_tokens] or NULL.  All-or-nothing; PKV_ENOBLOCKS counts the blocks
+ * this call takes off the free list (fresh ones and hits with count 0).
+ * Without prefix caching it behaves as pkv_seq_add.
+ */
+int pkv_seq_add_tokens(pkv_alloc* a, int64_t seq, const int32_t* tokens, int32_t num_tokens,
+                       int64_t* slots_out, int32_t* num_cached_out);
+
+/* pkv_seq_append / pkv_step_append with the new tokens' ids (host; tokens[i]
+ * belongs to seqs[i]).  A block such a token fills is entered in the cache.
+ * The plain calls append tokens of unknown id: the sequence then stops
+ * entering blocks. */
+int pkv_seq_append_token(pkv_alloc* a, int64_t seq, int32_t token, int64_t* slot_out,
+                         int32_t cow_out[2]);
+int pkv_step_append_tokens(pkv_alloc* a, const int64_t* seqs, const int32_t* tokens, int32_t n,
+                           int64_t* slots_out, int32_t* cow_pairs_out, int32_t* num_cow_out);
+
+/* Read-only lookup (the manager's get_cached_blocks(), section 03 reading
+ * (1)): the cached blocks a prompt of these ids would map.  blocks_out: host
+ * [num_tokens / block_size]; *num_blocks_out receives the count (0 when
+ * prefix caching is off).  Changes no counter. */
+int pkv_prefix_cache_lookup(const pkv_alloc* a, const int32_t* tokens, int32_t num_tokens,
+                            int32_t* blocks_out, int32_t* num_blocks_out);
+
+int pkv_prefix_cache_stats(const pkv_alloc* a, pkv_prefix_stats* out);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* pkv_last_error(void);
 

@@ -38,6 +38,41 @@ Readings taken where the pages are silent:
 * A batch step is all-or-nothing: if the pool cannot supply every block the
   step needs, nothing changes.  A step may not name one sequence twice.
 * Slot of position p in a sequence = table[p // B] * B + p % B.
+
+Prefix caching (optional, ``prefix_caching=True``), after page 3, section 04
+and section 03 reading (2):
+
+* A full block whose tokens are known is entered in a map from its key to its
+  physical block once the tokens that fill it have been given a slot; a later
+  prompt whose leading full blocks have the same keys maps those blocks
+  instead of computing them again (the page's two requests share a 16-token
+  system prompt: the second finds the first one's block and skips its
+  prefill).  The key of logical block i is the whole token prefix through the
+  end of block i, so two blocks share a key only when everything before them
+  matched too: the prefix-aware chain the page asks for, here without any
+  hash, hence without collisions.
+* Blocks stay in the map after their count drops to 0: they wait in the free
+  list, in release order, and a hit takes such a block back out of the list.
+  A block is evicted (leaves the map) only when the free list hands it out
+  again, so the least recently released block goes first, and a referenced
+  block is never evicted (page 3, section 04: evict under memory pressure,
+  LRU, never a referenced block).
+
+Readings taken where the pages are silent:
+
+* A prompt's lookup walks its full blocks from the first and stops at the
+  first miss; a prompt's partial last block is never looked up.
+* A prompt first takes back its hit blocks (those with count 0 leave the free
+  list), then takes fresh blocks from the free-list head, and then enters its
+  full, missed blocks in the map.  Blocks filled later by single appends are
+  entered when their last slot is handed out.
+* If a key is already in the map, the first block entered keeps it; the new
+  block stays out of the map.
+* A sequence keeps its token history only while every token it was given
+  came with an id; after an append without one, none of its later blocks is
+  entered.  A fork copies the parent's history.
+* Cache statistics count every full prompt block looked up (a query) and
+  every block found (a hit); the hit rate is hits / queries.
 """
 
 from __future__ import annotations
@@ -65,7 +100,8 @@ class BlockAllocatorModel:
     """Reference model of the host block allocator."""
 
     def __init__(self, num_blocks: int, block_size: int,
-                 free_order: Optional[Sequence[int]] = None):
+                 free_order: Optional[Sequence[int]] = None,
+                 prefix_caching: bool = False):
         if num_blocks <= 0 or block_size <= 0:
             raise AllocError(E_INVAL, "num_blocks and block_size must be positive")
         order = list(range(num_blocks)) if free_order is None else [int(b) for b in free_order]
@@ -75,8 +111,15 @@ class BlockAllocatorModel:
         self.block_size = block_size
         self.free: deque = deque(order)
         self.ref: List[int] = [0] * num_blocks
-        # seq id -> [block table (list of physical ids), number of tokens]
+        # seq id -> [block table (list of physical ids), number of tokens,
+        #            token history (list of ids) or None when unknown]
         self.seqs: Dict[int, list] = {}
+        self.prefix_caching = bool(prefix_caching)
+        self.cache: Dict[Tuple[int, ...], int] = {}   # prefix key -> block
+        self.block_key: Dict[int, Tuple[int, ...]] = {}
+        self.hits = 0
+        self.queries = 0
+        self.evictions = 0
 
     # ------------------------------------------------------------------ helpers
     def _no_blocks(self, needed: int) -> AllocError:
@@ -88,8 +131,28 @@ class BlockAllocatorModel:
 
     def _take(self) -> int:
         b = self.free.popleft()
+        key = self.block_key.pop(b, None)
+        if key is not None:          # the cached contents are about to be overwritten
+            del self.cache[key]
+            self.evictions += 1
         self.ref[b] = 1
         return b
+
+    def _enter(self, block: int, key: Tuple[int, ...]) -> None:
+        if self.prefix_caching and key not in self.cache:
+            self.cache[key] = block
+            self.block_key[block] = key
+
+    def _lookup(self, tokens: Sequence[int]) -> List[int]:
+        """Blocks holding the longest run of the prompt's leading full blocks."""
+        B = self.block_size
+        found: List[int] = []
+        for i in range(len(tokens) // B):
+            b = self.cache.get(tuple(tokens[:(i + 1) * B]))
+            if b is None:
+                break
+            found.append(b)
+        return found
 
     def _slot(self, table: List[int], pos: int) -> int:
         B = self.block_size
@@ -109,28 +172,72 @@ class BlockAllocatorModel:
         if needed > len(self.free):
             raise self._no_blocks(needed)
         table = [self._take() for _ in range(needed)]
-        self.seqs[seq] = [table, num_tokens]
+        self.seqs[seq] = [table, num_tokens, None]
         return [self._slot(table, p) for p in range(num_tokens)]
+
+    def add_tokens(self, seq: int, tokens: Sequence[int]) -> Tuple[List[int], int]:
+        """Admit a prompt given by its token ids.
+
+        With prefix caching, the prompt's leading full blocks found in the
+        cache are mapped instead of new ones (page 3, section 04).  Returns the
+        slot of every prompt position and the number of leading positions
+        whose K/V the cache already holds; only the positions after those
+        still have to be written.  All-or-nothing: the blocks taken out of the
+        free list (fresh ones, plus hits whose count was 0) are counted first.
+        """
+        tokens = [int(t) for t in tokens]
+        if seq in self.seqs:
+            raise AllocError(E_INVAL, f"bad add of sequence {seq}")
+        B = self.block_size
+        n = len(tokens)
+        hits = self._lookup(tokens) if self.prefix_caching else []
+        fresh = -(-n // B) - len(hits)
+        revived = sum(1 for b in hits if self.ref[b] == 0)
+        if fresh + revived > len(self.free):
+            raise self._no_blocks(fresh + revived)
+        if self.prefix_caching:
+            self.queries += n // B
+            self.hits += len(hits)
+        for b in hits:
+            if self.ref[b] == 0:
+                self.free.remove(b)
+            self.ref[b] += 1
+        table = hits + [self._take() for _ in range(fresh)]
+        for i in range(len(hits), n // B):
+            self._enter(table[i], tuple(tokens[:(i + 1) * B]))
+        self.seqs[seq] = [table, n, tokens]
+        return [self._slot(table, p) for p in range(n)], len(hits) * B
+
+    def cached_blocks(self, tokens: Sequence[int]) -> List[int]:
+        """Read-only lookup: the cached blocks a prompt of these tokens would
+        map (the manager's get_cached_blocks(), page 3, section 03 reading (1))."""
+        return self._lookup([int(t) for t in tokens]) if self.prefix_caching else []
+
+    def cache_stats(self) -> Dict[str, int]:
+        return {"hits": self.hits, "queries": self.queries,
+                "cached_blocks": len(self.cache), "evictions": self.evictions}
 
     def fork(self, parent: int, child: int) -> None:
         """``child`` starts as a copy of ``parent``'s table; every block gains a
         reference (page 1, section 4, step (1))."""
         if parent not in self.seqs or child in self.seqs:
             raise AllocError(E_INVAL, f"bad fork {parent} -> {child}")
-        table, length = self.seqs[parent]
+        table, length, toks = self.seqs[parent]
         for b in table:
             self.ref[b] += 1
-        self.seqs[child] = [list(table), length]
+        self.seqs[child] = [list(table), length, None if toks is None else list(toks)]
 
-    def append(self, seq: int) -> Tuple[int, Optional[Tuple[int, int]]]:
+    def append(self, seq: int, token: Optional[int] = None) -> Tuple[int, Optional[Tuple[int, int]]]:
         """Reserve the slot for one new token of ``seq``.
 
         Returns (slot, cow) where cow is (src, dst) when the shared last block
         had to be copied before this token is written into it, else None.
+        ``token`` (its id, optional) extends the sequence's history; with
+        prefix caching a block this token fills is entered in the cache.
         """
         if seq not in self.seqs:
             raise AllocError(E_INVAL, f"unknown sequence {seq}")
-        table, pos = self.seqs[seq]
+        table, pos, _ = self.seqs[seq]
         B = self.block_size
         cow = None
         if pos % B == 0:
@@ -149,24 +256,35 @@ class BlockAllocatorModel:
                 table[pos // B] = fresh
                 cow = (last, fresh)
         slot = self._slot(table, pos)
-        self.seqs[seq][1] = pos + 1
+        entry = self.seqs[seq]
+        entry[1] = pos + 1
+        if token is None:
+            entry[2] = None
+        elif entry[2] is not None:
+            entry[2].append(int(token))
+            if (pos + 1) % B == 0:
+                self._enter(table[pos // B], tuple(entry[2]))
         return slot, cow
 
-    def step(self, seqs: Iterable[int]) -> Tuple[List[int], List[Tuple[int, int]]]:
+    def step(self, seqs: Iterable[int], tokens: Optional[Sequence[int]] = None
+             ) -> Tuple[List[int], List[Tuple[int, int]]]:
         """One decode step: append one token to each sequence, in array order.
 
         All-or-nothing: the blocks the whole step takes are counted first, and
         if the pool holds fewer nothing changes.  For ``E_NOBLOCKS`` the message
-        names that count, the free count and the pool size.
+        names that count, the free count and the pool size.  ``tokens``, when
+        given, holds the id of each sequence's new token.
         """
         seqs = [int(s) for s in seqs]
+        if tokens is not None and len(tokens) != len(seqs):
+            raise AllocError(E_INVAL, "step: one token id per sequence")
         if len(set(seqs)) != len(seqs) or any(s not in self.seqs for s in seqs):
             raise AllocError(E_INVAL, "step names an unknown or repeated sequence")
         B = self.block_size
         ref = list(self.ref)
         needed = 0
         for s in seqs:
-            table, pos = self.seqs[s]
+            table, pos, _ = self.seqs[s]
             if pos % B == 0:
                 needed += 1
             elif ref[table[pos // B]] > 1:
@@ -176,8 +294,8 @@ class BlockAllocatorModel:
             raise self._no_blocks(needed)
         slots: List[int] = []
         pairs: List[Tuple[int, int]] = []
-        for s in seqs:
-            slot, cow = self.append(s)
+        for j, s in enumerate(seqs):
+            slot, cow = self.append(s, None if tokens is None else tokens[j])
             slots.append(slot)
             if cow is not None:
                 pairs.append(cow)
@@ -188,7 +306,7 @@ class BlockAllocatorModel:
         the first; a block whose count reaches 0 goes to the free-list tail."""
         if seq not in self.seqs:
             raise AllocError(E_INVAL, f"unknown sequence {seq}")
-        table, _ = self.seqs.pop(seq)
+        table = self.seqs.pop(seq)[0]
         for b in reversed(table):
             self.ref[b] -= 1
             if self.ref[b] == 0:
@@ -203,7 +321,7 @@ class BlockAllocatorModel:
 
     def filled(self, seq: int) -> List[int]:
         """'# filled' of each of the sequence's blocks (page 1, section 3(3))."""
-        table, n = self.seqs[seq]
+        table, n = self.seqs[seq][:2]
         B = self.block_size
         return [min(B, n - i * B) for i in range(len(table))]
 
@@ -214,7 +332,7 @@ class BlockAllocatorModel:
         for s in seqs:
             if s not in self.seqs:
                 raise AllocError(E_INVAL, f"unknown sequence {s}")
-            t, n = self.seqs[s]
+            t, n = self.seqs[s][:2]
             if len(t) > width:
                 raise AllocError(E_INVAL, f"sequence {s} holds {len(t)} blocks > width {width}")
             tables.append(list(t) + [pad] * (width - len(t)))

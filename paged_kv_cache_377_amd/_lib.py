@@ -48,6 +48,12 @@ class Stats(ctypes.Structure):
                 ("utilization", ctypes.c_double)]
 
 
+class PrefixStats(ctypes.Structure):
+    _fields_ = [("enabled", ctypes.c_int32), ("cached_blocks", ctypes.c_int32),
+                ("queries", ctypes.c_int64), ("hits", ctypes.c_int64),
+                ("evictions", ctypes.c_int64), ("hit_rate", ctypes.c_double)]
+
+
 _i32, _i64, _sz, _vp, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
 _P = ctypes.POINTER
 _SIGS = {
@@ -70,6 +76,12 @@ _SIGS = {
     "pkv_build_tables": (_i32, [_vp, _vp, _i32, _vp, _i32, _vp]),
     "pkv_alloc_stats": (_i32, [_vp, _P(Stats)]),
     "pkv_alloc_export": (_i32, [_vp, _vp, _vp, _vp]),
+    "pkv_prefix_cache_enable": (_i32, [_vp]),
+    "pkv_seq_add_tokens": (_i32, [_vp, _i64, _vp, _i32, _vp, _vp]),
+    "pkv_seq_append_token": (_i32, [_vp, _i64, _i32, _vp, _vp]),
+    "pkv_step_append_tokens": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp]),
+    "pkv_prefix_cache_lookup": (_i32, [_vp, _vp, _i32, _vp, _vp]),
+    "pkv_prefix_cache_stats": (_i32, [_vp, _P(PrefixStats)]),
     "pkv_last_error": (ctypes.c_char_p, []),
 }
 
@@ -244,7 +256,7 @@ class BlockAllocator:
     """Host block allocator (the library's pkv_alloc_* / pkv_seq_* calls)."""
 
     def __init__(self, num_blocks: int, block_size: int,
-                 free_order: Optional[Sequence[int]] = None):
+                 free_order: Optional[Sequence[int]] = None, prefix_caching: bool = False):
         self._l = lib()
         self.num_blocks = num_blocks
         self.block_size = block_size
@@ -258,6 +270,8 @@ class BlockAllocator:
         if not h:
             raise PagedKVError(PKV_EINVAL, self._l.pkv_last_error().decode())
         self._h = h
+        if prefix_caching:
+            _check(self._l.pkv_prefix_cache_enable(h))
 
     def close(self):
         if getattr(self, "_h", None):
@@ -272,23 +286,57 @@ class BlockAllocator:
         _check(self._l.pkv_seq_add(self._h, seq, num_tokens, slots.ctypes.data))
         return slots
 
+    def add_tokens(self, seq: int, tokens) -> Tuple[np.ndarray, int]:
+        """Admit a prompt by its token ids: (slots [n] int64, cached positions)."""
+        t = _np(tokens, np.int32)
+        slots = np.empty(t.size, dtype=np.int64)
+        cached = ctypes.c_int32()
+        _check(self._l.pkv_seq_add_tokens(self._h, seq, t.ctypes.data, t.size, slots.ctypes.data,
+                                          ctypes.byref(cached)))
+        return slots, cached.value
+
+    def cached_blocks(self, tokens) -> List[int]:
+        t = _np(tokens, np.int32)
+        out = np.empty(max(t.size // self.block_size, 1), dtype=np.int32)
+        n = ctypes.c_int32()
+        _check(self._l.pkv_prefix_cache_lookup(self._h, t.ctypes.data, t.size, out.ctypes.data,
+                                               ctypes.byref(n)))
+        return out[: n.value].tolist()
+
+    def cache_stats(self) -> dict:
+        st = PrefixStats()
+        _check(self._l.pkv_prefix_cache_stats(self._h, ctypes.byref(st)))
+        return {f: getattr(st, f) for f, _ in PrefixStats._fields_}
+
     def fork(self, parent: int, child: int) -> None:
         _check(self._l.pkv_seq_fork(self._h, parent, child))
 
-    def append(self, seq: int) -> Tuple[int, Optional[Tuple[int, int]]]:
+    def append(self, seq: int, token: Optional[int] = None) -> Tuple[int, Optional[Tuple[int, int]]]:
         slot = ctypes.c_int64()
         cow = (ctypes.c_int32 * 2)()
-        _check(self._l.pkv_seq_append(self._h, seq, ctypes.byref(slot), cow))
+        if token is None:
+            _check(self._l.pkv_seq_append(self._h, seq, ctypes.byref(slot), cow))
+        else:
+            _check(self._l.pkv_seq_append_token(self._h, seq, int(token), ctypes.byref(slot), cow))
         return slot.value, (None if cow[0] < 0 else (cow[0], cow[1]))
 
-    def step(self, seqs) -> Tuple[np.ndarray, np.ndarray]:
-        """Returns (slots [n] int64, copy pairs [k, 2] int32)."""
+    def step(self, seqs, tokens=None) -> Tuple[np.ndarray, np.ndarray]:
+        """Returns (slots [n] int64, copy pairs [k, 2] int32).  ``tokens``: the
+        new tokens' ids, one per sequence, or None."""
         s = _np(seqs, np.int64)
         slots = np.empty(s.size, dtype=np.int64)
         pairs = np.empty((max(s.size, 1), 2), dtype=np.int32)
         ncow = ctypes.c_int32()
-        _check(self._l.pkv_step_append(self._h, s.ctypes.data, s.size, slots.ctypes.data,
-                                       pairs.ctypes.data, ctypes.byref(ncow)))
+        if tokens is None:
+            _check(self._l.pkv_step_append(self._h, s.ctypes.data, s.size, slots.ctypes.data,
+                                           pairs.ctypes.data, ctypes.byref(ncow)))
+        else:
+            t = _np(tokens, np.int32)
+            if t.size != s.size:
+                raise PagedKVError(PKV_EINVAL, "step: one token id per sequence")
+            _check(self._l.pkv_step_append_tokens(self._h, s.ctypes.data, t.ctypes.data, s.size,
+                                                  slots.ctypes.data, pairs.ctypes.data,
+                                                  ctypes.byref(ncow)))
         return slots, pairs[: ncow.value].copy()
 
     def free(self, seq: int) -> None:

@@ -17,6 +17,25 @@
  * Where the pages are silent: the free list is a FIFO (take at the head,
  * return at the tail), a finished sequence releases its blocks last-to-first,
  * a batch step appends in array order and is all-or-nothing.
+ *
+ * Optional prefix caching (weishuz.com Month 2, section 04, and section 03
+ * reading (2): a map from block hash to block, reference counts, LRU
+ * eviction, a prefix-aware hash chain):
+ *   - the key of a full block is a 64-bit chain hash h_i = H(h_{i-1}, its B
+ *     token ids), so equal keys mean equal prefixes up to a collision; a hit
+ *     also compares the block's own ids and its parent hash, so a false hit
+ *     needs a 64-bit collision of two different prefixes' chain hashes;
+ *   - a full block is entered when the tokens that fill it get their slots
+ *     (prompt blocks at admission, later blocks by appends that carry ids);
+ *     the first block entered under a key keeps it;
+ *   - a block whose count drops to 0 keeps its entry and waits in the free
+ *     list, which is doubly linked so a hit can take it back out; the free
+ *     list hands out its head, evicting the entry of a cached block, so the
+ *     least recently released block is evicted first and a referenced one
+ *     never is;
+ *   - a prompt's lookup walks its full blocks from the first and stops at the
+ *     first miss; the prompt takes back its hits, then takes fresh blocks,
+ *     then enters its missed full blocks.
  */
 #include <stdarg.h>
 #include <stdint.h>
@@ -63,13 +82,19 @@ typedef struct {
   int32_t* blocks;   /* block table, logical -> physical                   */
   uint32_t stamp;    /* last batch step that named this sequence           */
   uint8_t state;     /* 0 empty, 1 live, 2 deleted                         */
+  uint8_t tracked;   /* token ids known for every position (prefix cache)  */
+  uint64_t chain;    /* chain hash through the last full block             */
+  int32_t* toks;     /* ids of the partial last block's tokens, [B]        */
 } seq_entry;
 
 struct pkv_alloc {
   int32_t num_blocks;
   int32_t block_size;
-  int32_t* fifo;     /* ring buffer of free ids, capacity num_blocks       */
-  int32_t head;
+  /* free list, doubly linked in release order (-1 ends it) */
+  int32_t* nxt;
+  int32_t* prv;
+  int32_t fhead;
+  int32_t ftail;
   int32_t nfree;
   int32_t* ref;
   int32_t* touched;  /* scratch for a step's dry run, capacity num_blocks  */
@@ -78,6 +103,18 @@ struct pkv_alloc {
   size_t nlive;
   size_t nused;      /* live + deleted                                     */
   uint32_t step_no;
+  /* prefix cache (all NULL / 0 while disabled) */
+  int prefix;
+  uint64_t* bkey;    /* chain hash of each cached block                    */
+  uint64_t* bpar;    /* chain hash of the prefix before it                 */
+  int32_t* btok;     /* [num_blocks][B] ids of each cached block            */
+  uint8_t* bcached;
+  int32_t* map;      /* linear-probing table of block ids, -1 empty        */
+  size_t mcap;       /* power of two >= 2 * num_blocks                     */
+  int32_t ncached;
+  int64_t hits;
+  int64_t queries;
+  int64_t evictions;
 };
 
 static uint64_t mix64(uint64_t x) {
@@ -138,6 +175,8 @@ static seq_entry* insert(pkv_alloc* a, int64_t id) {
 static void erase(pkv_alloc* a, seq_entry* e) {
   free(e->blocks);
   e->blocks = NULL;
+  free(e->toks);
+  e->toks = NULL;
   e->state = 2;
   a->nlive--;
 }
@@ -153,19 +192,105 @@ static int reserve_blocks(seq_entry* e, int32_t n) {
   return PKV_OK;
 }
 
-static int32_t take_block(pkv_alloc* a) {
-  int32_t b = a->fifo[a->head];
-  a->head = (a->head + 1 == a->num_blocks) ? 0 : a->head + 1;
+/* ------------------------------------------------------- prefix cache */
+
+static const uint64_t kChainSeed = 0x6a09e667f3bcc908ULL;  /* h_{-1} */
+static const uint64_t kGolden = 0x9e3779b97f4a7c15ULL;
+
+/* Chain hash of one full block: parent hash, then the block's ids in order,
+ * each folded in through the 64-bit finaliser above. */
+static uint64_t chain_hash(uint64_t parent, const int32_t* t, int32_t n) {
+  uint64_t h = mix64(parent ^ kGolden);
+  for (int32_t i = 0; i < n; ++i) h = mix64(h ^ ((uint64_t)(uint32_t)t[i] + kGolden * (uint64_t)(i + 1)));
+  return h;
+}
+
+/* Map slot holding the block cached under (key, parent, ids), or the empty
+ * slot where the probe ended (*found = 0). */
+static size_t map_probe(const pkv_alloc* a, uint64_t key, uint64_t parent, const int32_t* t,
+                        int* found) {
+  const size_t mask = a->mcap - 1;
+  const int32_t B = a->block_size;
+  for (size_t i = (size_t)mix64(key) & mask;; i = (i + 1) & mask) {
+    int32_t b = a->map[i];
+    if (b < 0) {
+      *found = 0;
+      return i;
+    }
+    if (a->bkey[b] == key && a->bpar[b] == parent &&
+        memcmp(a->btok + (size_t)b * B, t, (size_t)B * sizeof(int32_t)) == 0) {
+      *found = 1;
+      return i;
+    }
+  }
+}
+
+static int32_t map_find(const pkv_alloc* a, uint64_t key, uint64_t parent, const int32_t* t) {
+  int found;
+  size_t i = map_probe(a, key, parent, t, &found);
+  return found ? a->map[i] : -1;
+}
+
+/* Enter block b (full, just filled) under the chain hash of its ids. */
+static void cache_enter(pkv_alloc* a, int32_t b, uint64_t key, uint64_t parent, const int32_t* t) {
+  int found;
+  size_t i = map_probe(a, key, parent, t, &found);
+  if (found) return; /* the first block entered under a key keeps it */
+  const int32_t B = a->block_size;
+  a->map[i] = b;
+  a->bkey[b] = key;
+  a->bpar[b] = parent;
+  memcpy(a->btok + (size_t)b * B, t, (size_t)B * sizeof(int32_t));
+  a->bcached[b] = 1;
+  a->ncached++;
+}
+
+/* Remove block b's entry (linear probing: shift later entries back). */
+static void cache_evict(pkv_alloc* a, int32_t b) {
+  const size_t mask = a->mcap - 1;
+  size_t i = (size_t)mix64(a->bkey[b]) & mask;
+  while (a->map[i] != b) i = (i + 1) & mask;
+  size_t hole = i;
+  for (size_t j = (hole + 1) & mask; a->map[j] >= 0; j = (j + 1) & mask) {
+    size_t home = (size_t)mix64(a->bkey[a->map[j]]) & mask;
+    /* move map[j] into the hole unless its home lies cyclically in (hole, j] */
+    int stays = (hole <= j) ? (home > hole && home <= j) : (home > hole || home <= j);
+    if (!stays) {
+      a->map[hole] = a->map[j];
+      hole = j;
+    }
+  }
+  a->map[hole] = -1;
+  a->bcached[b] = 0;
+  a->ncached--;
+  a->evictions++;
+}
+
+/* ----------------------------------------------------------- free list */
+
+static void free_unlink(pkv_alloc* a, int32_t b) {
+  int32_t p = a->prv[b], n = a->nxt[b];
+  if (p >= 0) a->nxt[p] = n; else a->fhead = n;
+  if (n >= 0) a->prv[n] = p; else a->ftail = p;
+  a->nxt[b] = a->prv[b] = -1;
   a->nfree--;
-  a->ref[b] = 1;
-  return b;
 }
 
 static void return_block(pkv_alloc* a, int32_t b) {
-  int64_t tail = (int64_t)a->head + a->nfree;
-  if (tail >= a->num_blocks) tail -= a->num_blocks;
-  a->fifo[tail] = b;
+  a->prv[b] = a->ftail;
+  a->nxt[b] = -1;
+  if (a->ftail >= 0) a->nxt[a->ftail] = b; else a->fhead = b;
+  a->ftail = b;
   a->nfree++;
+}
+
+/* Hand out the free-list head; its cached contents, if any, are evicted. */
+static int32_t take_block(pkv_alloc* a) {
+  int32_t b = a->fhead;
+  free_unlink(a, b);
+  if (a->prefix && a->bcached[b]) cache_evict(a, b);
+  a->ref[b] = 1;
+  return b;
 }
 
 static int no_blocks(const pkv_alloc* a, int64_t needed) {
@@ -184,12 +309,18 @@ pkv_alloc* pkv_alloc_create(int32_t num_blocks, int32_t block_size, const int32_
   if (!a) goto oom;
   a->num_blocks = num_blocks;
   a->block_size = block_size;
-  a->fifo = (int32_t*)malloc((size_t)num_blocks * sizeof(int32_t));
+  a->nxt = (int32_t*)malloc((size_t)num_blocks * sizeof(int32_t));
+  a->prv = (int32_t*)malloc((size_t)num_blocks * sizeof(int32_t));
+  int32_t* order = (int32_t*)malloc((size_t)num_blocks * sizeof(int32_t));
   a->ref = (int32_t*)calloc((size_t)num_blocks, sizeof(int32_t));
   a->touched = (int32_t*)malloc((size_t)num_blocks * sizeof(int32_t));
   a->tcap = 64;
   a->tab = (seq_entry*)calloc(a->tcap, sizeof(seq_entry));
-  if (!a->fifo || !a->ref || !a->touched || !a->tab) goto oom;
+  a->fhead = a->ftail = -1;
+  if (!a->nxt || !a->prv || !order || !a->ref || !a->touched || !a->tab) {
+    free(order);
+    goto oom;
+  }
   if (free_order) {
     /* must be a permutation: use ref[] as a seen-mark, then clear it */
     for (int32_t i = 0; i < num_blocks; ++i) {
@@ -197,18 +328,20 @@ pkv_alloc* pkv_alloc_create(int32_t num_blocks, int32_t block_size, const int32_
       if (b < 0 || b >= num_blocks || a->ref[b]) {
         pkv__fail(PKV_EINVAL, "free_order is not a permutation of 0..%d (entry %d = %d)",
                   num_blocks - 1, i, b);
+        free(order);
         pkv_alloc_destroy(a);
         return NULL;
       }
       a->ref[b] = 1;
-      a->fifo[i] = b;
+      order[i] = b;
     }
     memset(a->ref, 0, (size_t)num_blocks * sizeof(int32_t));
   } else {
-    for (int32_t i = 0; i < num_blocks; ++i) a->fifo[i] = i;
+    for (int32_t i = 0; i < num_blocks; ++i) order[i] = i;
   }
-  a->head = 0;
-  a->nfree = num_blocks;
+  a->nfree = 0;
+  for (int32_t i = 0; i < num_blocks; ++i) return_block(a, order[i]);
+  free(order);
   return a;
 oom:
   pkv__fail(PKV_EINVAL, "out of host memory");
@@ -220,12 +353,45 @@ void pkv_alloc_destroy(pkv_alloc* a) {
   if (!a) return;
   if (a->tab)
     for (size_t i = 0; i < a->tcap; ++i)
-      if (a->tab[i].state == 1) free(a->tab[i].blocks);
+      if (a->tab[i].state == 1) {
+        free(a->tab[i].blocks);
+        free(a->tab[i].toks);
+      }
   free(a->tab);
-  free(a->fifo);
+  free(a->nxt);
+  free(a->prv);
   free(a->ref);
   free(a->touched);
+  free(a->bkey);
+  free(a->bpar);
+  free(a->btok);
+  free(a->bcached);
+  free(a->map);
   free(a);
+}
+
+int pkv_prefix_cache_enable(pkv_alloc* a) {
+  pkv__clear_error();
+  if (!a) return pkv__fail(PKV_EINVAL, "allocator handle is NULL");
+  if (a->prefix) return PKV_OK;
+  if (a->nlive) return pkv__fail(PKV_EINVAL, "prefix caching must be enabled before any sequence is added");
+  const size_t n = (size_t)a->num_blocks;
+  size_t cap = 16;
+  while (cap < 2 * n) cap *= 2;
+  a->bkey = (uint64_t*)calloc(n, sizeof(uint64_t));
+  a->bpar = (uint64_t*)calloc(n, sizeof(uint64_t));
+  a->btok = (int32_t*)calloc(n * (size_t)a->block_size, sizeof(int32_t));
+  a->bcached = (uint8_t*)calloc(n, 1);
+  a->map = (int32_t*)malloc(cap * sizeof(int32_t));
+  if (!a->bkey || !a->bpar || !a->btok || !a->bcached || !a->map) {
+    free(a->bkey); free(a->bpar); free(a->btok); free(a->bcached); free(a->map);
+    a->bkey = a->bpar = NULL; a->btok = a->map = NULL; a->bcached = NULL;
+    return pkv__fail(PKV_EINVAL, "out of host memory");
+  }
+  for (size_t i = 0; i < cap; ++i) a->map[i] = -1;
+  a->mcap = cap;
+  a->prefix = 1;
+  return PKV_OK;
 }
 
 static int64_t slot_of(const pkv_alloc* a, const seq_entry* e, int32_t pos) {
@@ -255,6 +421,117 @@ int pkv_seq_add(pkv_alloc* a, int64_t seq, int32_t num_tokens, int64_t* slots_ou
   return PKV_OK;
 }
 
+/* Walk the prompt's full blocks through the cache: the leading blocks found
+ * go to hits[] (at most num_tokens / B), the chain hash through the last
+ * full block to *chain_out.  Returns the number of hits. */
+static int32_t prefix_walk(const pkv_alloc* a, const int32_t* tokens, int32_t num_tokens,
+                           int32_t* hits, uint64_t* chain_out) {
+  const int32_t B = a->block_size;
+  const int32_t full = num_tokens / B;
+  uint64_t h = kChainSeed;
+  int32_t nhit = 0;
+  int walking = a->prefix;
+  for (int32_t i = 0; i < full; ++i) {
+    const int32_t* t = tokens + (size_t)i * B;
+    uint64_t k = chain_hash(h, t, B);
+    if (walking) {
+      int32_t b = map_find(a, k, h, t);
+      if (b >= 0) hits[nhit++] = b; else walking = 0;
+      if (nhit == a->num_blocks) walking = 0; /* hits[] holds num_blocks ids at most */
+    }
+    h = k;
+  }
+  *chain_out = h;
+  return nhit;
+}
+
+int pkv_seq_add_tokens(pkv_alloc* a, int64_t seq, const int32_t* tokens, int32_t num_tokens,
+                       int64_t* slots_out, int32_t* num_cached_out) {
+  pkv__clear_error();
+  if (!a) return pkv__fail(PKV_EINVAL, "allocator handle is NULL");
+  if (num_tokens < 0) return pkv__fail(PKV_EINVAL, "num_tokens %d < 0", num_tokens);
+  if (num_tokens > 0 && !tokens) return pkv__fail(PKV_EINVAL, "tokens is NULL");
+  if (find(a, seq)) return pkv__fail(PKV_EINVAL, "sequence %lld already exists", (long long)seq);
+  const int32_t B = a->block_size;
+  const int32_t need = (int32_t)(((int64_t)num_tokens + B - 1) / B);
+  const int32_t full = num_tokens / B;
+  /* hits are staged in the step scratch (capacity num_blocks >= need) */
+  int32_t* hits = a->touched;
+  uint64_t chain = kChainSeed;
+  int32_t nhit = 0;
+  if (a->prefix) nhit = prefix_walk(a, tokens, num_tokens, hits, &chain);
+  int32_t revived = 0;
+  for (int32_t i = 0; i < nhit; ++i) revived += a->ref[hits[i]] == 0;
+  const int32_t fresh = need - nhit;
+  if ((int64_t)fresh + revived > a->nfree) return no_blocks(a, (int64_t)fresh + revived);
+  seq_entry* e = insert(a, seq);
+  if (!e) return PKV_EINVAL;
+  if (reserve_blocks(e, need) != PKV_OK) {
+    erase(a, e);
+    return PKV_EINVAL;
+  }
+  if (a->prefix) {
+    e->toks = (int32_t*)malloc((size_t)B * sizeof(int32_t));
+    if (!e->toks) {
+      erase(a, e);
+      return pkv__fail(PKV_EINVAL, "out of host memory");
+    }
+  }
+  /* from here on nothing fails */
+  for (int32_t i = 0; i < nhit; ++i) {
+    int32_t b = hits[i];
+    if (a->ref[b] == 0) free_unlink(a, b);
+    a->ref[b]++;
+    e->blocks[i] = b;
+  }
+  for (int32_t i = nhit; i < need; ++i) e->blocks[i] = take_block(a);
+  e->nblk = need;
+  e->len = num_tokens;
+  if (a->prefix) {
+    a->queries += full;
+    a->hits += nhit;
+    uint64_t h = kChainSeed;
+    for (int32_t i = 0; i < full; ++i) {
+      const int32_t* t = tokens + (size_t)i * B;
+      uint64_t k = chain_hash(h, t, B);
+      if (i >= nhit) cache_enter(a, e->blocks[i], k, h, t);
+      h = k;
+    }
+    e->tracked = 1;
+    e->chain = chain;
+    memcpy(e->toks, tokens + (size_t)full * B, (size_t)(num_tokens - full * B) * sizeof(int32_t));
+  }
+  if (slots_out)
+    for (int32_t p = 0; p < num_tokens; ++p) slots_out[p] = slot_of(a, e, p);
+  if (num_cached_out) *num_cached_out = nhit * B;
+  return PKV_OK;
+}
+
+int pkv_prefix_cache_lookup(const pkv_alloc* a, const int32_t* tokens, int32_t num_tokens,
+                            int32_t* blocks_out, int32_t* num_blocks_out) {
+  pkv__clear_error();
+  if (!a) return pkv__fail(PKV_EINVAL, "allocator handle is NULL");
+  if (num_tokens < 0 || (num_tokens > 0 && !tokens) || !num_blocks_out)
+    return pkv__fail(PKV_EINVAL, "bad lookup arguments");
+  if (num_tokens / a->block_size > 0 && !blocks_out)
+    return pkv__fail(PKV_EINVAL, "blocks_out is NULL");
+  uint64_t chain;
+  *num_blocks_out = a->prefix ? prefix_walk(a, tokens, num_tokens, blocks_out, &chain) : 0;
+  return PKV_OK;
+}
+
+int pkv_prefix_cache_stats(const pkv_alloc* a, pkv_prefix_stats* out) {
+  pkv__clear_error();
+  if (!a || !out) return pkv__fail(PKV_EINVAL, "NULL argument");
+  out->enabled = a->prefix;
+  out->cached_blocks = a->ncached;
+  out->queries = a->queries;
+  out->hits = a->hits;
+  out->evictions = a->evictions;
+  out->hit_rate = a->queries ? (double)a->hits / (double)a->queries : 0.0;
+  return PKV_OK;
+}
+
 int pkv_seq_fork(pkv_alloc* a, int64_t parent, int64_t child) {
   pkv__clear_error();
   if (!a) return pkv__fail(PKV_EINVAL, "allocator handle is NULL");
@@ -268,6 +545,16 @@ int pkv_seq_fork(pkv_alloc* a, int64_t parent, int64_t child) {
   if (reserve_blocks(c, p->nblk) != PKV_OK) {
     erase(a, c);
     return PKV_EINVAL;
+  }
+  if (p->tracked) {
+    c->toks = (int32_t*)malloc((size_t)a->block_size * sizeof(int32_t));
+    if (!c->toks) {
+      erase(a, c);
+      return pkv__fail(PKV_EINVAL, "out of host memory");
+    }
+    memcpy(c->toks, p->toks, (size_t)a->block_size * sizeof(int32_t));
+    c->tracked = 1;
+    c->chain = p->chain;
   }
   if (p->nblk) memcpy(c->blocks, p->blocks, (size_t)p->nblk * sizeof(int32_t));
   c->nblk = p->nblk;
@@ -284,8 +571,11 @@ static int append_needs(const pkv_alloc* a, const seq_entry* e) {
 }
 
 /* Append one token; the caller has checked that a block is available when
- * append_needs() says so.  Writes the slot and the copy pair (or -1, -1). */
-static int append_one(pkv_alloc* a, seq_entry* e, int64_t* slot_out, int32_t* cow) {
+ * append_needs() says so.  Writes the slot and the copy pair (or -1, -1).
+ * `token` points at the token's id, or is NULL when the id is unknown (the
+ * sequence then stops feeding the prefix cache). */
+static int append_one(pkv_alloc* a, seq_entry* e, int64_t* slot_out, int32_t* cow,
+                      const int32_t* token) {
   int32_t pos = e->len, B = a->block_size;
   cow[0] = -1;
   cow[1] = -1;
@@ -304,10 +594,21 @@ static int append_one(pkv_alloc* a, seq_entry* e, int64_t* slot_out, int32_t* co
   }
   *slot_out = slot_of(a, e, pos);
   e->len = pos + 1;
+  if (!token) {
+    e->tracked = 0;
+  } else if (e->tracked) {
+    e->toks[pos % B] = *token;
+    if ((pos + 1) % B == 0) {
+      uint64_t k = chain_hash(e->chain, e->toks, B);
+      cache_enter(a, e->blocks[pos / B], k, e->chain, e->toks);
+      e->chain = k;
+    }
+  }
   return PKV_OK;
 }
 
-int pkv_seq_append(pkv_alloc* a, int64_t seq, int64_t* slot_out, int32_t cow_out[2]) {
+static int seq_append(pkv_alloc* a, int64_t seq, int64_t* slot_out, int32_t cow_out[2],
+                      const int32_t* token) {
   pkv__clear_error();
   if (!a) return pkv__fail(PKV_EINVAL, "allocator handle is NULL");
   if (!slot_out) return pkv__fail(PKV_EINVAL, "slot_out is NULL");
@@ -317,7 +618,7 @@ int pkv_seq_append(pkv_alloc* a, int64_t seq, int64_t* slot_out, int32_t cow_out
   if (append_needs(a, e) > a->nfree) return no_blocks(a, 1);
   if (e->len % a->block_size == 0 && reserve_blocks(e, e->nblk + 1) != PKV_OK) return PKV_EINVAL;
   int32_t cow[2];
-  int rc = append_one(a, e, slot_out, cow);
+  int rc = append_one(a, e, slot_out, cow, token);
   if (rc == PKV_OK && cow_out) {
     cow_out[0] = cow[0];
     cow_out[1] = cow[1];
@@ -325,8 +626,17 @@ int pkv_seq_append(pkv_alloc* a, int64_t seq, int64_t* slot_out, int32_t cow_out
   return rc;
 }
 
-int pkv_step_append(pkv_alloc* a, const int64_t* seqs, int32_t n, int64_t* slots_out,
-                    int32_t* cow_pairs_out, int32_t* num_cow_out) {
+int pkv_seq_append(pkv_alloc* a, int64_t seq, int64_t* slot_out, int32_t cow_out[2]) {
+  return seq_append(a, seq, slot_out, cow_out, NULL);
+}
+
+int pkv_seq_append_token(pkv_alloc* a, int64_t seq, int32_t token, int64_t* slot_out,
+                         int32_t cow_out[2]) {
+  return seq_append(a, seq, slot_out, cow_out, &token);
+}
+
+static int step_append(pkv_alloc* a, const int64_t* seqs, const int32_t* tokens, int32_t n,
+                       int64_t* slots_out, int32_t* cow_pairs_out, int32_t* num_cow_out) {
   pkv__clear_error();
   if (!a) return pkv__fail(PKV_EINVAL, "allocator handle is NULL");
   if (n < 0) return pkv__fail(PKV_EINVAL, "n %d < 0", n);
@@ -372,7 +682,7 @@ int pkv_step_append(pkv_alloc* a, const int64_t* seqs, int32_t n, int64_t* slots
   for (int32_t i = 0; i < n; ++i) {
     seq_entry* e = find(a, seqs[i]);
     int32_t cow[2];
-    append_one(a, e, &slots_out[i], cow);
+    append_one(a, e, &slots_out[i], cow, tokens ? &tokens[i] : NULL);
     if (cow[0] >= 0) {
       cow_pairs_out[2 * ncow] = cow[0];
       cow_pairs_out[2 * ncow + 1] = cow[1];
@@ -381,6 +691,20 @@ int pkv_step_append(pkv_alloc* a, const int64_t* seqs, int32_t n, int64_t* slots
   }
   if (num_cow_out) *num_cow_out = ncow;
   return PKV_OK;
+}
+
+int pkv_step_append(pkv_alloc* a, const int64_t* seqs, int32_t n, int64_t* slots_out,
+                    int32_t* cow_pairs_out, int32_t* num_cow_out) {
+  return step_append(a, seqs, NULL, n, slots_out, cow_pairs_out, num_cow_out);
+}
+
+int pkv_step_append_tokens(pkv_alloc* a, const int64_t* seqs, const int32_t* tokens, int32_t n,
+                           int64_t* slots_out, int32_t* cow_pairs_out, int32_t* num_cow_out) {
+  if (n > 0 && !tokens) {
+    pkv__clear_error();
+    return pkv__fail(PKV_EINVAL, "tokens is NULL");
+  }
+  return step_append(a, seqs, tokens, n, slots_out, cow_pairs_out, num_cow_out);
 }
 
 int pkv_seq_free(pkv_alloc* a, int64_t seq) {
@@ -466,12 +790,10 @@ int pkv_alloc_export(const pkv_alloc* a, int32_t* free_fifo_out, int32_t* num_fr
                      int32_t* ref_cnt_out) {
   pkv__clear_error();
   if (!a) return pkv__fail(PKV_EINVAL, "allocator handle is NULL");
-  if (free_fifo_out)
-    for (int32_t i = 0; i < a->nfree; ++i) {
-      int64_t j = (int64_t)a->head + i;
-      if (j >= a->num_blocks) j -= a->num_blocks;
-      free_fifo_out[i] = a->fifo[j];
-    }
+  if (free_fifo_out) {
+    int32_t i = 0;
+    for (int32_t b = a->fhead; b >= 0; b = a->nxt[b]) free_fifo_out[i++] = b;
+  }
   if (num_free_out) *num_free_out = a->nfree;
   if (ref_cnt_out) memcpy(ref_cnt_out, a->ref, (size_t)a->num_blocks * sizeof(int32_t));
   return PKV_OK;

@@ -23,64 +23,54 @@ namespace {
 constexpr int kThreads = 256;
 
 // One thread per 16-byte piece of the [T, Hkv, D] input.  `row_chunks` is
-// D * elem_bytes / 16 and `rows` = T * Hkv.
+// D * elem_bytes / 16 and `total_chunks` = T * Hkv * row_chunks < 2^31 (the
+// host checks), so the index arithmetic stays in 32 bits.
 __global__ __launch_bounds__(kThreads) void kv_write_kernel(
     const uint4* __restrict__ k, const uint4* __restrict__ v,
     const int64_t* __restrict__ slot_mapping, uint4* __restrict__ k_cache,
-    uint4* __restrict__ v_cache, int32_t num_kv_heads, int32_t block_size,
-    int32_t row_chunks, int64_t total_chunks, int64_t num_slots) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    uint4* __restrict__ v_cache, uint32_t num_kv_heads, uint32_t block_size,
+    uint32_t row_chunks, uint32_t total_chunks, int64_t num_slots) {
+  const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
   if (i >= total_chunks) return;
-  const int32_t c = (int32_t)(i % row_chunks);
-  const int64_t row = i / row_chunks;
-  const int32_t h = (int32_t)(row % num_kv_heads);
-  const int64_t t = row / num_kv_heads;
+  const uint32_t row = i / row_chunks;
+  const uint32_t c = i - row * row_chunks;
+  const uint32_t t = row / num_kv_heads;
+  const uint32_t h = row - t * num_kv_heads;
   const int64_t slot = slot_mapping[t];
+  uint4 kv = k[i];
+  uint4 vv = v[i];
+  // The row loads do not depend on the slot: the empty asm needs their values
+  // before the slot test, so all three loads are in flight together instead
+  // of the row loads waiting for the slot.
+  asm volatile("" : "+v"(kv.x), "+v"(kv.y), "+v"(kv.z), "+v"(kv.w), "+v"(vv.x), "+v"(vv.y),
+               "+v"(vv.z), "+v"(vv.w));
   if (slot < 0 || slot >= num_slots) return;
   const int64_t blk = slot / block_size;
   const int64_t off = slot - blk * block_size;
   const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * row_chunks + c;
-  const uint4 kv = k[i];
-  const uint4 vv = v[i];
   k_cache[dst] = kv;
   v_cache[dst] = vv;
 }
 
-// Grid: num_pairs * groups_per_block workgroups; each workgroup copies
-// kThreads * kPerThread pieces of one block's K and V run.
-constexpr int kPerThread = 4;
-
+// Grid: num_pairs * groups_per_block workgroups; each thread copies one
+// 16-byte piece of one block's K run and the same piece of its V run.  One
+// piece per thread, held in registers: with several pieces per thread in a
+// private array the compiler moved the array to LDS and scratch, and the copy
+// ran about three times slower.
 __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
     uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
     const int32_t* __restrict__ pairs, int32_t block_chunks, int32_t groups_per_block,
     int32_t num_blocks) {
   const int32_t pair = blockIdx.x / groups_per_block;
   const int32_t grp = blockIdx.x - pair * groups_per_block;
+  const int32_t c = grp * kThreads + threadIdx.x;
   const int32_t src = pairs[2 * pair];
   const int32_t dst = pairs[2 * pair + 1];
-  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-  const uint4* ks = k_cache + (int64_t)src * block_chunks;
-  const uint4* vs = v_cache + (int64_t)src * block_chunks;
-  uint4* kd = k_cache + (int64_t)dst * block_chunks;
-  uint4* vd = v_cache + (int64_t)dst * block_chunks;
-  const int32_t base = grp * (kThreads * kPerThread) + threadIdx.x;
-  uint4 kr[kPerThread], vr[kPerThread];
-#pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    const int32_t c = base + j * kThreads;
-    if (c < block_chunks) {
-      kr[j] = ks[c];
-      vr[j] = vs[c];
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    const int32_t c = base + j * kThreads;
-    if (c < block_chunks) {
-      kd[c] = kr[j];
-      vd[c] = vr[j];
-    }
-  }
+  if (c >= block_chunks || src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  const uint4 kr = k_cache[(int64_t)src * block_chunks + c];
+  const uint4 vr = v_cache[(int64_t)src * block_chunks + c];
+  k_cache[(int64_t)dst * block_chunks + c] = kr;
+  v_cache[(int64_t)dst * block_chunks + c] = vr;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -108,12 +98,15 @@ extern "C" int pkv_paged_kv_write(const void* k, const void* v, const int64_t* s
     return pkv__fail(PKV_EINVAL, "device pointers must be 16-byte aligned (slot_mapping 8-byte)");
   const int32_t row_chunks = (int32_t)(row_bytes / 16);
   const int64_t total = (int64_t)num_tokens * c->num_kv_heads * row_chunks;
+  if (total > INT32_MAX)
+    return pkv__fail(PKV_EINVAL, "write of %lld 16-byte pieces is too large (limit 2^31 - 1)",
+                     (long long)total);
   const int64_t grid = (total + kThreads - 1) / kThreads;
-  if (grid > INT32_MAX) return pkv__fail(PKV_EINVAL, "write too large");
   hipLaunchKernelGGL(kv_write_kernel, dim3((uint32_t)grid), dim3(kThreads), 0,
                      (hipStream_t)stream, (const uint4*)k, (const uint4*)v, slot_mapping,
-                     (uint4*)k_cache, (uint4*)v_cache, c->num_kv_heads, c->block_size,
-                     row_chunks, total, (int64_t)c->num_blocks * c->block_size);
+                     (uint4*)k_cache, (uint4*)v_cache, (uint32_t)c->num_kv_heads,
+                     (uint32_t)c->block_size, (uint32_t)row_chunks, (uint32_t)total,
+                     (int64_t)c->num_blocks * c->block_size);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return pkv__fail(PKV_EHIP, "kv_write launch: %s", hipGetErrorString(e));
   return PKV_OK;
@@ -135,8 +128,7 @@ extern "C" int pkv_copy_blocks(void* k_cache, void* v_cache, const pkv_cache_des
     return pkv__fail(PKV_EUNSUPPORTED, "block of %lld bytes is not a multiple of 16",
                      (long long)block_bytes);
   const int32_t block_chunks = (int32_t)(block_bytes / 16);
-  const int32_t per_group = kThreads * kPerThread;
-  const int32_t groups = (block_chunks + per_group - 1) / per_group;
+  const int32_t groups = (block_chunks + kThreads - 1) / kThreads;
   const int64_t grid = (int64_t)num_pairs * groups;
   if (grid > INT32_MAX) return pkv__fail(PKV_EINVAL, "copy too large");
   hipLaunchKernelGGL(copy_blocks_kernel, dim3((uint32_t)grid), dim3(kThreads), 0,

@@ -72,3 +72,44 @@ def check(world: ContentWorld, tables: Dict[int, List[int]], lens: Dict[int, int
     used = {b for b in range(N) if ref[b] > 0}
     assert used.isdisjoint(free) and used | set(free) == set(range(N)), \
         "free list and referenced blocks partition the pool"
+
+
+class PrefixWorld(ContentWorld):
+    """Slot memory for prefix caching.  A position's K/V depend on every token
+    up to it, so each written slot holds the whole token prefix through its
+    position, and ``hist[seq][p]`` is the prefix a correct table must show at
+    position p.  Positions the allocator reports as already cached are not
+    written: they must already hold the right prefix, put there by an earlier
+    sequence."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        super().__init__(num_blocks, block_size)
+        self.tokens: Dict[int, List[int]] = {}
+
+    def on_add_tokens(self, seq: int, tokens: List[int], slots: List[int], cached: int):
+        prefixes = [tuple(tokens[:p + 1]) for p in range(len(tokens))]
+        for p in range(cached, len(tokens)):
+            self.mem[slots[p]] = prefixes[p]
+        self.hist[seq] = prefixes
+        self.tokens[seq] = list(tokens)
+
+    def on_fork(self, parent: int, child: int):
+        super().on_fork(parent, child)
+        self.tokens[child] = list(self.tokens[parent])
+
+    def on_append_token(self, seq: int, token: int, slot: int):
+        self.tokens[seq].append(token)
+        pre = tuple(self.tokens[seq])
+        self.mem[slot] = pre
+        self.hist[seq].append(pre)
+
+    def on_free(self, seq: int):
+        super().on_free(seq)
+        del self.tokens[seq]
+
+    def block_holds(self, block: int, key) -> bool:
+        """Block ``block`` holds the K/V of the last full block of prefix ``key``."""
+        B = self.B
+        i = len(key) // B - 1
+        return len(key) % B == 0 and all(
+            self.mem.get(block * B + o) == tuple(key[:i * B + o + 1]) for o in range(B))

@@ -1,10 +1,13 @@
 /* Replays an allocator op stream read from stdin and prints every result, so
  * the allocator can run under AddressSanitizer / UBSan in a plain gcc build.
  * Input lines:  N B perm...  then  add s n | fork p c | append s |
- *               step k s1..sk | free s | table s
+ *               step k s1..sk | free s | table s | prefix |
+ *               addt s k t1..tk | appt s t | stept k s1..sk t1..tk |
+ *               look k t1..tk
  * Output: one line per op with the return code and results. */
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include "pagedkv.h"
 
@@ -19,7 +22,61 @@ int main(void) {
   if (!a) return 3;
   char op[16];
   while (scanf("%15s", op) == 1) {
-    if (op[0] == 'a' && op[1] == 'd') {
+    if (strcmp(op, "prefix") == 0) {
+      printf("prefix %d\n", pkv_prefix_cache_enable(a));
+    } else if (strcmp(op, "addt") == 0) {
+      long long s; int k;
+      if (scanf("%lld %d", &s, &k) != 2 || k < 0) return 2;
+      int32_t* t = malloc(sizeof(int32_t) * (k > 0 ? k : 1));
+      for (int i = 0; i < k; ++i) if (scanf("%d", &t[i]) != 1) return 2;
+      int64_t* slots = malloc(sizeof(int64_t) * (k > 0 ? k : 1));
+      int32_t cached = -7;
+      int rc = pkv_seq_add_tokens(a, s, t, k, slots, &cached);
+      printf("addt %d", rc);
+      if (rc == 0) {
+        printf(" %d :", cached);
+        for (int i = 0; i < k; ++i) printf(" %lld", (long long)slots[i]);
+      }
+      printf("\n");
+      free(t); free(slots);
+    } else if (strcmp(op, "appt") == 0) {
+      long long s; int tok; int64_t slot; int32_t cow[2];
+      if (scanf("%lld %d", &s, &tok) != 2) return 2;
+      int rc = pkv_seq_append_token(a, s, tok, &slot, cow);
+      if (rc == 0) printf("appt 0 %lld %d %d\n", (long long)slot, cow[0], cow[1]);
+      else printf("appt %d\n", rc);
+    } else if (strcmp(op, "stept") == 0) {
+      int k;
+      if (scanf("%d", &k) != 1 || k < 0) return 2;
+      int64_t* ids = malloc(sizeof(int64_t) * (k > 0 ? k : 1));
+      int32_t* toks = malloc(sizeof(int32_t) * (k > 0 ? k : 1));
+      int64_t* slots = malloc(sizeof(int64_t) * (k > 0 ? k : 1));
+      int32_t* pairs = malloc(sizeof(int32_t) * 2 * (k > 0 ? k : 1));
+      for (int i = 0; i < k; ++i) { long long x; if (scanf("%lld", &x) != 1) return 2; ids[i] = x; }
+      for (int i = 0; i < k; ++i) if (scanf("%d", &toks[i]) != 1) return 2;
+      int32_t nc = 0;
+      int rc = pkv_step_append_tokens(a, ids, toks, k, slots, pairs, &nc);
+      printf("stept %d", rc);
+      if (rc == 0) {
+        for (int i = 0; i < k; ++i) printf(" %lld", (long long)slots[i]);
+        printf(" |");
+        for (int i = 0; i < nc; ++i) printf(" %d %d", pairs[2 * i], pairs[2 * i + 1]);
+      }
+      printf("\n");
+      free(ids); free(toks); free(slots); free(pairs);
+    } else if (strcmp(op, "look") == 0) {
+      int k;
+      if (scanf("%d", &k) != 1 || k < 0) return 2;
+      int32_t* t = malloc(sizeof(int32_t) * (k > 0 ? k : 1));
+      for (int i = 0; i < k; ++i) if (scanf("%d", &t[i]) != 1) return 2;
+      int32_t* blocks = malloc(sizeof(int32_t) * (k / b > 0 ? k / b : 1));
+      int32_t nb = -1;
+      int rc = pkv_prefix_cache_lookup(a, t, k, blocks, &nb);
+      printf("look %d", rc);
+      if (rc == 0) for (int i = 0; i < nb; ++i) printf(" %d", blocks[i]);
+      printf("\n");
+      free(t); free(blocks);
+    } else if (op[0] == 'a' && op[1] == 'd') {
       long long s; int k;
       if (scanf("%lld %d", &s, &k) != 2) return 2;
       int64_t* slots = malloc(sizeof(int64_t) * (k > 0 ? k : 1));
@@ -88,6 +145,11 @@ int main(void) {
   printf("\n");
   pkv_stats st;
   pkv_alloc_stats(a, &st);
+  pkv_prefix_stats ps;
+  pkv_prefix_cache_stats(a, &ps);
+  if (ps.enabled)
+    printf("cache %lld %lld %d %lld\n", (long long)ps.hits, (long long)ps.queries, ps.cached_blocks,
+           (long long)ps.evictions);
   free(fifo); free(ref);
   pkv_alloc_destroy(a);
   return 0;

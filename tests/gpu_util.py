@@ -57,3 +57,28 @@ def check_close(out_bits: np.ndarray, ref: np.ndarray, dtype: str, where=None):
     big = np.abs(ref) >= 0.2
     max_rel = float((err[big] / np.abs(ref[big])).max()) if big.any() else 0.0
     return float(err.max()) if err.size else 0.0, max_rel
+
+
+def scatter_histories(pool_shape, dtype: str, tables, lens, hist_k, hist_v, B: int):
+    """Expected pools: token t of sequence i at block tables[i][t // B], offset
+    t % B; every other slot 0."""
+    import datagen
+
+    kc = np.zeros(pool_shape, dtype=datagen.np_dtype(dtype))
+    vc = np.zeros(pool_shape, dtype=datagen.np_dtype(dtype))
+    for i, n in enumerate(lens):
+        n = int(n)
+        t = np.arange(n)
+        blk = np.asarray(tables[i])[t // B]
+        kc[blk, :, t % B, :] = hist_k[i][:n]
+        vc[blk, :, t % B, :] = hist_v[i][:n]
+    return kc, vc
+
+
+def live_rows(pool: np.ndarray, tables, lens, B: int) -> np.ndarray:
+    """Rows [tokens, Hkv, D] of every sequence's live slots, concatenated."""
+    rows = []
+    for i, n in enumerate(lens):
+        t = np.arange(int(n))
+        rows.append(pool[np.asarray(tables[i])[t // B], :, t % B, :])
+    return np.concatenate(rows)

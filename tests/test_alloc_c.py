@@ -184,8 +184,8 @@ def _replay_lines(seed):
     return lines, B, N, order
 
 
-def _oracle_replay(lines, B, N, order):
-    o = BlockAllocatorModel(N, B, order)
+def _oracle_replay(lines, B, N, order, model=None):
+    o = BlockAllocatorModel(N, B, order) if model is None else model
     out = []
     for ln in lines[1:]:
         f = ln.split()
@@ -235,6 +235,88 @@ def replay_bin(tmp_path_factory):
     if r.returncode != 0:
         pytest.skip("sanitizer build unavailable: " + r.stderr[-400:])
     return exe
+
+
+def _prefix_replay_lines(seed):
+    rnd = random.Random(500 + seed)
+    B = rnd.choice([1, 2, 4])
+    N = rnd.randrange(3, 24)
+    order = rnd.sample(range(N), N)
+    alpha = rnd.choice([2, 3])
+    ids = list(range(12))
+    lines = [f"{N} {B} " + " ".join(map(str, order)), "prefix"]
+    for _ in range(400):
+        r = rnd.random()
+        s = rnd.choice(ids)
+        toks = [rnd.randrange(alpha) for _ in range(rnd.randint(0, 4 * B + 1))]
+        if r < 0.25:
+            lines.append(f"addt {s} {len(toks)} " + " ".join(map(str, toks)))
+        elif r < 0.3:
+            lines.append(f"add {s} {rnd.randint(0, 2 * B)}")
+        elif r < 0.38:
+            lines.append(f"fork {s} {rnd.choice(ids)}")
+        elif r < 0.5:
+            lines.append(f"appt {s} {rnd.randrange(alpha)}")
+        elif r < 0.55:
+            lines.append(f"append {s}")
+        elif r < 0.75:
+            k = rnd.randint(0, 5)
+            batch = [rnd.choice(ids) for _ in range(k)]
+            tt = [rnd.randrange(alpha) for _ in range(k)]
+            lines.append(f"stept {k} " + " ".join(map(str, batch + tt)))
+        elif r < 0.85:
+            lines.append(f"free {s}")
+        elif r < 0.92:
+            lines.append(f"look {len(toks)} " + " ".join(map(str, toks)))
+        else:
+            lines.append(f"table {s}")
+    return lines, B, N, order
+
+
+def _oracle_prefix_replay(lines, B, N, order):
+    o = BlockAllocatorModel(N, B, order, prefix_caching=True)
+    out = ["prefix 0"]
+    plain = _oracle_replay
+    for ln in lines[2:]:
+        f = ln.split()
+        try:
+            if f[0] == "addt":
+                k = int(f[2])
+                slots, cached = o.add_tokens(int(f[1]), [int(x) for x in f[3:3 + k]])
+                out.append(f"addt 0 {cached} :" + "".join(f" {x}" for x in slots))
+            elif f[0] == "appt":
+                slot, cow = o.append(int(f[1]), int(f[2]))
+                cow = cow or (-1, -1)
+                out.append(f"appt 0 {slot} {cow[0]} {cow[1]}")
+            elif f[0] == "stept":
+                k = int(f[1])
+                seqs = [int(x) for x in f[2:2 + k]]
+                toks = [int(x) for x in f[2 + k:2 + 2 * k]]
+                slots, pairs = o.step(seqs, toks)
+                out.append("stept 0" + "".join(f" {x}" for x in slots) + " |" +
+                           "".join(f" {a} {b}" for a, b in pairs))
+            elif f[0] == "look":
+                k = int(f[1])
+                out.append("look 0" + "".join(f" {b}" for b in o.cached_blocks([int(x) for x in f[2:2 + k]])))
+            else:
+                out.extend(plain([lines[0], ln], B, N, order, model=o)[:-1])
+        except AllocError as e:
+            out.append(f"{f[0]} {e.code}")
+    out.append("final free" + "".join(f" {b}" for b in o.free_list()) + " | ref" +
+               "".join(f" {r}" for r in o.ref_counts()))
+    st = o.cache_stats()
+    out.append(f"cache {st['hits']} {st['queries']} {st['cached_blocks']} {st['evictions']}")
+    return out
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_sanitizer_replay_prefix_cache_matches_oracle(replay_bin, seed):
+    lines, B, N, order = _prefix_replay_lines(seed)
+    r = subprocess.run([replay_bin], input="\n".join(lines) + "\n", capture_output=True,
+                       text=True, timeout=60)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "ERROR: AddressSanitizer" not in r.stderr and "runtime error" not in r.stderr
+    assert r.stdout.strip().splitlines() == _oracle_prefix_replay(lines, B, N, order)
 
 
 @pytest.mark.parametrize("seed", range(12))
