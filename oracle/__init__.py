@@ -26,12 +26,13 @@ Modules:
   allocator   block pool + per-sequence block tables (free list, ref counts,
               lazy allocation, fork, copy-on-write, free)
   cache_ops   slot_mapping write and block copy, on raw bit patterns
-  attention   decode attention over K/V gathered through the block table
+  attention   decode and causal prefill attention over K/V gathered through
+              the block table
 """
 
 from .allocator import AllocError, BlockAllocatorModel, E_INVAL, E_NOBLOCKS
 from .cache_ops import copy_blocks, paged_kv_write
-from .attention import paged_attention_decode, to_f64
+from .attention import paged_attention_decode, paged_attention_prefill, to_f64
 
 __all__ = [
     "AllocError",
@@ -41,5 +42,6 @@ __all__ = [
     "copy_blocks",
     "paged_kv_write",
     "paged_attention_decode",
+    "paged_attention_prefill",
     "to_f64",
 ]

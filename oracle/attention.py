@@ -23,6 +23,19 @@ For sequence s with n = context_lens[s] tokens and query head h:
 and out = 0 when n = 0.  Slots at positions >= n and blocks the table does not
 reach are never read, so whatever bits they hold (NaN included) cannot reach
 the result.
+
+Prefill (several new tokens per sequence; page 1, section 3(3), step 1): the
+prompt's tokens are computed together and their K/V are filled into the
+sequence's blocks.  Reading taken: the new tokens are the last n_new of the
+sequence's n = context_lens[s] tokens (their K/V written before the
+attention, as in decode), and new token j, at position p = n - n_new + j,
+attends causally to every position t <= p:
+
+  out[j] = sum_{t <= p} exp(l_t - max_{u <= p} l_u) V_t / sum_{t <= p} exp(...)
+
+With one new token per sequence this is the decode above; with earlier
+positions already cached (prefix caching, or a prompt split into chunks) the
+new tokens still see the whole prefix through the table.
 """
 
 from __future__ import annotations
@@ -75,4 +88,48 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens,
             logits = scale * (K @ qh)                           # [n]
             w = np.exp(logits - logits.max())
             out[s, h, :] = (w @ V) / w.sum()
+    return out
+
+
+def paged_attention_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+                            scale: float, dtype: str, seqs=None, heads=None):
+    """fp64 causal attention of new tokens over their paged context.
+
+    q: [T, Hq, D], the new tokens of all sequences packed in sequence order;
+    query_start_loc: [S + 1], sequence s owns rows query_start_loc[s] ..
+    query_start_loc[s + 1] - 1.  Returns out[T, Hq, D] (fp64); rows of
+    sequences outside ``seqs`` stay 0.
+    """
+    T, Hq, D = q.shape
+    _, Hkv, B, _ = k_cache.shape
+    if Hq % Hkv != 0:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    G = Hq // Hkv
+    S = len(context_lens)
+    qsl = [int(x) for x in query_start_loc]
+    if len(qsl) != S + 1 or qsl[0] != 0 or qsl[-1] != T or any(b < a for a, b in zip(qsl, qsl[1:])):
+        raise ValueError("query_start_loc must run from 0 to T without decreasing")
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    seq_list = range(S) if seqs is None else seqs
+    head_list = range(Hq) if heads is None else heads
+    for s in seq_list:
+        n = int(context_lens[s])
+        n_new = qsl[s + 1] - qsl[s]
+        if n_new > n:
+            raise ValueError(f"sequence {s}: {n_new} new tokens but context {n}")
+        if n_new == 0:
+            continue
+        first = n - n_new
+        blocks = [int(block_tables[s][t // B]) for t in range(n)]
+        offsets = [t % B for t in range(n)]
+        for h in head_list:
+            g = h // G
+            K = to_f64(k_cache[blocks, g, offsets, :], dtype)   # [n, D]
+            V = to_f64(v_cache[blocks, g, offsets, :], dtype)
+            for j in range(n_new):
+                p = first + j
+                qh = to_f64(q[qsl[s] + j, h, :], dtype)
+                logits = scale * (K[: p + 1] @ qh)
+                w = np.exp(logits - logits.max())
+                out[qsl[s] + j, h, :] = (w @ V[: p + 1]) / w.sum()
     return out
