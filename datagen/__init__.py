@@ -20,6 +20,10 @@ Workloads (all values N(0, 1); bf16 carried as uint16 bit patterns):
   5  mixed      256 seqs, context floor(exp(U(ln 16, ln 8192))) clipped to
                 [16, 8192], 64 q / 8 kv heads, head_dim 128, bf16,
                 block size 8, 16 or 32, one step of 256 appended tokens
+  6  prefix     64 requests = one 1024-token system prompt + U{16..1024}
+                own tokens (token ids from a 32000-id vocabulary), heads as 2
+  7  prefill    16 seqs = cached prefix U{0..2048} + a 512-token chunk of
+                new tokens, heads as 2
 
 Random draws come from numpy's PCG64 generator seeded with 1000 + workload
 number, in this order: context lengths, free-list permutation, q, K pool, V
@@ -98,6 +102,7 @@ SHAPES = {
     4: Shape(8, 32, 8, 128, 16, "bf16", 1.0 / math.sqrt(128), 512),
     5: Shape(256, 64, 8, 128, 16, "bf16", 1.0 / math.sqrt(128), 512),
     6: Shape(64, 32, 8, 128, 16, "bf16", 1.0 / math.sqrt(128), 512),
+    7: Shape(16, 32, 8, 128, 16, "bf16", 1.0 / math.sqrt(128), 512),
 }
 
 
@@ -304,3 +309,39 @@ def prefix_plan(seed: Optional[int] = None, num_requests: int = 64, system_len: 
     nb = int(math.ceil(1.25 * need)) + spare_blocks
     order = rng.permutation(nb).astype(np.int32)
     return PrefixPlan(sh, system, suffixes, nb, order)
+
+
+@dataclass
+class PrefillInputs:
+    """Chunked-prefill workload: every sequence has a cached prefix and a
+    chunk of new tokens whose K/V are already in the pool (placement of the
+    tokens in blocks is left to an allocator, from ``free_order``)."""
+    shape: Shape
+    context_lens: np.ndarray          # [S] int32, prefix + chunk
+    qsl: np.ndarray                   # [S + 1] int32, query_start_loc
+    num_blocks: int
+    free_order: np.ndarray
+    q: np.ndarray                     # [T, Hq, D]
+    k_cache: np.ndarray               # [NB, Hkv, B, D]
+    v_cache: np.ndarray
+
+
+def prefill_inputs(seed: Optional[int] = None, num_seqs: int = 16, chunk: int = 512,
+                   max_prefix: int = 2048, block_size: int = 16) -> PrefillInputs:
+    """16 sequences = a cached prefix of U{0..2048} tokens + a 512-token chunk,
+    Llama-3-8B layer shape; a pool 1.25x the blocks needed, its free order a
+    seeded permutation."""
+    sh = shape(7, block_size)
+    sh.num_seqs = num_seqs
+    rng = np.random.default_rng(seed_for(7) if seed is None else seed)
+    prefix = rng.integers(0, max_prefix, size=num_seqs, endpoint=True)
+    ctx = (prefix + chunk).astype(np.int32)
+    B = sh.block_size
+    need = int(sum(-(-int(n) // B) for n in ctx))
+    nb = int(math.ceil(1.25 * need))
+    order = rng.permutation(nb).astype(np.int32)
+    q = normal(rng, (num_seqs * chunk, sh.num_q_heads, sh.head_dim), sh.dtype)
+    kc = normal(rng, (nb, sh.num_kv_heads, B, sh.head_dim), sh.dtype)
+    vc = normal(rng, (nb, sh.num_kv_heads, B, sh.head_dim), sh.dtype)
+    qsl = np.arange(num_seqs + 1, dtype=np.int32) * chunk
+    return PrefillInputs(sh, ctx, qsl, nb, order, q, kc, vc)

@@ -10,6 +10,7 @@
  *   pkv_paged_kv_write          write new tokens' K/V into their slots
  *   pkv_copy_blocks             copy whole blocks (copy-on-write of shared blocks)
  *   pkv_paged_attention_decode  one-query-per-sequence attention through the table
+ *   pkv_paged_attention_prefill causal attention of several new tokens per sequence
  *   pkv_alloc_* / pkv_seq_*     free list, ref counts, lazy allocation, fork, CoW
  *
  * Conventions common to every call:
@@ -166,6 +167,45 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
                                int32_t partition_size, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/*
+ * Causal attention of several new tokens per sequence over the sequence's
+ * paged context (blog section 3(3), step 1: a prompt's tokens are processed
+ * together and their K/V are filled into the sequence's blocks; the K/V of
+ * the new tokens are written with pkv_paged_kv_write before this call).
+ * Sequence s owns query rows query_start_loc[s] .. query_start_loc[s+1] - 1:
+ * its n_new new tokens, the last n_new of its n = context_lens[s] tokens.  New
+ * token j (position p = n - n_new + j) and query head h (KV head h / G) give
+ *   out[row, h, :] = sum_{t <= p} softmax_t(scale * <q[row, h, :], K_t>) V_t
+ * with K_t, V_t read through the table as in decode.  One new token per
+ * sequence is the decode; tokens before the new ones may come from the prefix
+ * cache or from earlier chunks of the same prompt.  Computed on MFMA with
+ * fp32 accumulation; each softmax weight enters the V product as two bf16
+ * parts (bf16(p) and bf16 of the remainder, nearest even), and the output is
+ * rounded to bf16 (nearest even).
+ *
+ *   out, q           device, [num_tokens, num_q_heads, head_dim] bf16
+ *   block_tables     device, [num_seqs, max_blocks_per_seq] int32, as in decode
+ *   context_lens     device, [num_seqs] int32, each in [n_new, max_context_len]
+ *   query_start_loc  device, [num_seqs + 1] int32, non-decreasing, from 0 to
+ *                    at most num_tokens
+ *   max_new_tokens   host int, >= every n_new (sizes the launch)
+ *   max_context_len  host int, >= every context_lens[s]
+ * Positions after a row's own never affect it; slots at positions >= n and
+ * blocks the table does not reach are never used.  Bad device-side contents
+ * (n_new > n, table entries outside the pool) never lead to an access
+ * outside the arrays; the result is then unspecified.  Only bf16 caches,
+ * head_dim in {64, 128}, block_size in {8, 16, 32} and query heads per KV
+ * head in {1, 2, 4, 8, 16} are built; other shapes return PKV_EUNSUPPORTED.
+ * Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP.
+ */
+int pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,
+                                const void* v_cache, const pkv_cache_desc* c,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, const int32_t* query_start_loc,
+                                int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                int32_t max_new_tokens, int32_t max_context_len, float scale,
+                                void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Host-side contract checks (synchronous, for debugging; no GPU needed).    */
 /* Each takes HOST copies of the index arrays and returns PKV_OK, PKV_ERANGE */
@@ -178,6 +218,12 @@ int pkv_validate_write(const int64_t* slot_mapping, int32_t num_tokens,
 /* ids in range, dsts distinct, no dst is a src */
 int pkv_validate_copy(const int32_t* src_dst_pairs, int32_t num_pairs,
                       const pkv_cache_desc* c);
+/* query_start_loc runs from 0 to <= num_tokens without decreasing, every
+ * n_new <= max_new_tokens and <= its context length, plus the decode checks */
+int pkv_validate_prefill(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, const int32_t* query_start_loc,
+                         int32_t num_seqs, int32_t num_tokens, int32_t max_new_tokens,
+                         int32_t max_context_len, const pkv_cache_desc* c);
 /* 0 <= ctx <= max_context_len, ceil(ctx/B) <= width, read entries in range */
 int pkv_validate_decode(const int32_t* block_tables, int32_t max_blocks_per_seq,
                         const int32_t* context_lens, int32_t num_seqs,

@@ -1,5 +1,6 @@
-"""MI355X-native paged KV cache: decode attention, slot_mapping write, block
-copy and host block allocator, behind the C ABI of include/pagedkv.h.
+"""MI355X-native paged KV cache: decode and causal prefill attention,
+slot_mapping write, block copy and host block allocator (with prefix
+caching), behind the C ABI of include/pagedkv.h.
 
 The Python layer is a thin ctypes binding over ``libpagedkv.so`` (built
 in-tree for gfx950 by ``python -m paged_kv_cache_377_amd.build``); it loads
@@ -25,8 +26,10 @@ from ._lib import (  # noqa: F401
     header_functions,
     lib,
     paged_attention_decode,
+    paged_attention_prefill,
     paged_kv_write,
     validate_copy,
     validate_decode,
+    validate_prefill,
     validate_write,
 )

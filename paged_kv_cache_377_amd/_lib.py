@@ -62,6 +62,9 @@ _SIGS = {
     "pkv_decode_workspace_bytes": (_sz, [_P(CacheDesc), _i32, _i32, _i32, _i32]),
     "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _P(CacheDesc), _vp, _i32, _vp, _i32,
                                           _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
+    "pkv_paged_attention_prefill": (_i32, [_vp, _vp, _vp, _vp, _P(CacheDesc), _vp, _i32, _vp, _vp,
+                                           _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
+    "pkv_validate_prefill": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _P(CacheDesc)]),
     "pkv_validate_write": (_i32, [_vp, _i32, _P(CacheDesc)]),
     "pkv_validate_copy": (_i32, [_vp, _i32, _P(CacheDesc)]),
     "pkv_validate_decode": (_i32, [_vp, _i32, _vp, _i32, _i32, _P(CacheDesc)]),
@@ -222,6 +225,30 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         _stream(stream)))
 
 
+def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens,
+                            query_start_loc, scale: float, max_new_tokens: int,
+                            max_context_len: int, stream=None) -> None:
+    """out, q: [T, Hq, D] bf16 (the new tokens of all sequences, packed);
+    block_tables: [S, M] int32; context_lens: [S] int32; query_start_loc:
+    [S + 1] int32.  ``max_new_tokens`` / ``max_context_len`` are host-side
+    bounds of the per-sequence new-token counts and context lengths."""
+    torch = _torch()
+    T, Hq, D = q.shape
+    if out.shape != q.shape or out.dtype != q.dtype or q.dtype != k_cache.dtype:
+        raise PagedKVError(PKV_EINVAL, "out/q/cache dtype or shape mismatch")
+    if (block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32
+            or query_start_loc.dtype != torch.int32):
+        raise PagedKVError(PKV_EINVAL, "block_tables, context_lens and query_start_loc must be int32")
+    S = context_lens.numel()
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or query_start_loc.numel() != S + 1:
+        raise PagedKVError(PKV_EINVAL, "block_tables must be [S, M] and query_start_loc [S + 1]")
+    desc = cache_desc(k_cache)
+    _check(lib().pkv_paged_attention_prefill(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), _ptr(query_start_loc), S, T, Hq,
+        int(max_new_tokens), int(max_context_len), float(scale), _stream(stream)))
+
+
 # --------------------------------------------------------- host checks
 
 def _np(a, dtype):
@@ -248,6 +275,19 @@ def validate_decode(block_tables, context_lens, max_context_len: int, desc: Cach
     width = t.shape[1] if t.ndim == 2 else 0
     _check(lib().pkv_validate_decode(t.ctypes.data, width, c.ctypes.data, c.size,
                                      int(max_context_len), ctypes.byref(desc)))
+
+
+def validate_prefill(block_tables, context_lens, query_start_loc, num_tokens: int,
+                     max_new_tokens: int, max_context_len: int, desc: CacheDesc) -> None:
+    t = _np(block_tables, np.int32)
+    c = _np(context_lens, np.int32)
+    qs = _np(query_start_loc, np.int32)
+    if qs.size != c.size + 1:
+        raise PagedKVError(PKV_EINVAL, "query_start_loc must have num_seqs + 1 entries")
+    width = t.shape[1] if t.ndim == 2 else 0
+    _check(lib().pkv_validate_prefill(t.ctypes.data, width, c.ctypes.data, qs.ctypes.data, c.size,
+                                      int(num_tokens), int(max_new_tokens), int(max_context_len),
+                                      ctypes.byref(desc)))
 
 
 # ------------------------------------------------------------ allocator

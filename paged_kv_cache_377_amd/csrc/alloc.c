@@ -880,3 +880,26 @@ int pkv_validate_decode(const int32_t* block_tables, int32_t width, const int32_
   }
   return PKV_OK;
 }
+
+int pkv_validate_prefill(const int32_t* block_tables, int32_t width, const int32_t* context_lens,
+                         const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens,
+                         int32_t max_new_tokens, int32_t max_context_len, const pkv_cache_desc* c) {
+  pkv__clear_error();
+  if (num_seqs < 0 || num_tokens < 0 || (num_seqs >= 0 && !query_start_loc))
+    return pkv__fail(PKV_EINVAL, "bad query_start_loc arguments");
+  if (query_start_loc[0] != 0)
+    return pkv__fail(PKV_ERANGE, "query_start_loc[0] = %d, not 0", query_start_loc[0]);
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    int32_t a = query_start_loc[s], b = query_start_loc[s + 1];
+    if (b < a || b > num_tokens)
+      return pkv__fail(PKV_ERANGE, "query_start_loc[%d] = %d after %d (num_tokens %d)", s + 1, b,
+                       a, num_tokens);
+    if (b - a > max_new_tokens)
+      return pkv__fail(PKV_ERANGE, "sequence %d has %d new tokens > max_new_tokens %d", s, b - a,
+                       max_new_tokens);
+    if (context_lens && b - a > context_lens[s])
+      return pkv__fail(PKV_ERANGE, "sequence %d has %d new tokens but context %d", s, b - a,
+                       context_lens[s]);
+  }
+  return pkv_validate_decode(block_tables, width, context_lens, num_seqs, max_context_len, c);
+}

@@ -1,0 +1,427 @@
+// Causal paged prefill attention for gfx950: several new tokens per sequence
+// attend to their whole context through the block table, on MFMA (bf16 in,
+// fp32 accumulation, bf16 out).
+//
+// What is computed (PagedAttention blog, 0539edu.com, section 3(3), step 1:
+// the prompt's tokens are processed together and their K/V are filled into
+// the sequence's blocks; read as causal attention over the prompt): sequence
+// s owns query rows query_start_loc[s] .. query_start_loc[s + 1] - 1, its
+// n_new new tokens, which are the last n_new of its context_lens[s] tokens
+// (their K/V are written before this call, as for decode).  New token j sits
+// at position p = context_lens[s] - n_new + j and attends to every position
+// t <= p, keys and values read from block block_tables[s][t / B], offset
+// t % B.  Query head h reads KV head h / G.
+//
+// Work decomposition.  A workgroup (4 waves) owns one KV head g of one
+// sequence and 128 (token, head) rows: 128 / G consecutive new tokens times
+// the G query heads that share g, token-major.  Each wave owns 32 rows as two
+// 16-column MFMA tiles.  Keys are walked in tiles of 32 from position 0 to
+// the tile's last position; each K/V tile is copied from HBM into LDS once
+// per workgroup (rows in natural [key][dim] order) and read by all 4 waves,
+// double-buffered so the next tile's loads are in flight during the MFMAs.
+//
+// Per key tile and wave:
+//   S^T = K Q^T    (A = 16 keys x 32 dims of K from LDS, B = 32 dims x 16
+//                   rows of Q held in registers): 2 key halves x D/32 steps
+//                   x 2 column tiles of v_mfma_f32_16x16x32_bf16;
+//   online softmax per row (a row is an MFMA column: lanes with equal l % 16
+//                   hold its 8 keys of the tile), base-2 exponent, causal
+//                   mask by position, lazy rescale;
+//   O^T += V^T P^T (A = 16 dims x 32 keys of V^T, B = 32 keys x 16 rows of
+//                   P): D/16 steps x 2 column tiles x 2 parts of P.  The B
+//                   operand is the lane's own 8 probabilities in the order
+//                   the S^T tiles left them; the A operand takes V in the
+//                   same key order with the LDS transpose read
+//                   (ds_read_b64_tr_b16), two per step.
+// The probabilities enter the PV product as two bf16 parts, hi = bf16(p)
+// and lo = bf16(p - hi) (round to nearest even), one MFMA each with the same
+// V operand: a single bf16 rounding of p moves a row's output by up to
+// 2^-9 |V|, which for rows that cancel is above the accuracy asked of this
+// path; hi + lo carries p to about 2^-17.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "pkv_internal.h"
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerWave = 32;                      // two 16-column MFMA tiles
+constexpr int kRowsPerGroup = kWaves * kRowsPerWave;  // 128 (token, head) rows
+constexpr int kKeys = 32;                             // keys per K/V tile
+
+// A tile's row maximum must exceed the reference maximum by more than this
+// (log2 units) before that row's accumulators are rescaled; weights <= 2^8.
+constexpr float kRescaleSlack = 8.0f;
+
+// D = A B + C on a 16x16x32 bf16 tile.  Lane l supplies row (l % 16) of A and
+// column (l % 16) of B, each as 8 consecutive k-slots of group l / 16; it
+// receives D[4 (l / 16) + r][l % 16] in element r.
+__device__ inline f32x4_t mfma16x16x32(const uint4& a, const uint4& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ inline uint32_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ inline float bf16_value(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Max / sum over the four 16-lane groups of the wave (lanes with equal
+// l % 16), with the VALU row-swap instructions.
+__device__ inline float rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ inline float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// LDS row pitch of a staged K or V tile, in 16-bit elements: D plus 8 (16 B)
+// of padding, so the 16 rows one MFMA operand read touches start in
+// different banks.
+template <int D>
+struct Pitch {
+  static constexpr int kElems = D + 8;
+  static constexpr int kTile = kKeys * kElems;  // elements per staged matrix
+};
+
+// One thread's share of staging a K/V tile: D / 64 pieces of 16 bytes of K
+// and the same of V (a tile is 32 rows of D bf16 = 4 D pieces per matrix).
+template <int D>
+struct Stage {
+  static constexpr int kPer = D / 64;
+  uint4 k[kPer], v[kPer];
+};
+
+template <int D>
+__device__ inline void stage_load(Stage<D>& st, const uint16_t* __restrict__ k_cache,
+                                  const uint16_t* __restrict__ v_cache,
+                                  const int32_t* __restrict__ table, int t0, int n, int log2b,
+                                  int g, int num_kv_heads, int num_blocks) {
+  constexpr int kChunks = D / 8;  // 16-byte pieces per key row
+#pragma unroll
+  for (int u = 0; u < Stage<D>::kPer; ++u) {
+    const int idx = threadIdx.x + kThreads * u;
+    const int key = idx / kChunks;
+    const int c = idx - key * kChunks;
+    const int t = t0 + key;
+    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+    if (t < n) {
+      const int phys = table[t >> log2b];
+      if (phys >= 0 && phys < num_blocks) {
+        const int64_t row = ((int64_t)phys * num_kv_heads + g) * ((int64_t)1 << log2b) +
+                            (t & ((1 << log2b) - 1));
+        kv = *reinterpret_cast<const uint4*>(k_cache + row * D + 8 * c);
+        vv = *reinterpret_cast<const uint4*>(v_cache + row * D + 8 * c);
+      }
+    }
+    st.k[u] = kv;
+    st.v[u] = vv;
+  }
+}
+
+template <int D>
+__device__ inline void stage_store(const Stage<D>& st, uint16_t* lk, uint16_t* lv) {
+  constexpr int kChunks = D / 8;
+#pragma unroll
+  for (int u = 0; u < Stage<D>::kPer; ++u) {
+    const int idx = threadIdx.x + kThreads * u;
+    const int key = idx / kChunks;
+    const int c = idx - key * kChunks;
+    *reinterpret_cast<uint4*>(lk + key * Pitch<D>::kElems + 8 * c) = st.k[u];
+    *reinterpret_cast<uint4*>(lv + key * Pitch<D>::kElems + 8 * c) = st.v[u];
+  }
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(
+    uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
+    const int32_t* __restrict__ block_tables, int32_t max_blocks_per_seq,
+    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start_loc,
+    int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t num_blocks, int32_t log2b, int32_t max_context_len, int32_t tiles_per_seq,
+    float qscale) {
+  constexpr int kTokens = kRowsPerGroup / G;  // new tokens per workgroup
+  constexpr int KK = D / 32;                  // k-steps of the QK product
+  constexpr int DT = D / 16;                  // 16-dim tiles of the output
+
+  __shared__ __align__(16) uint16_t lds[2][2][Pitch<D>::kTile];  // [buffer][K, V]
+
+  // Heaviest tiles (last new tokens, most keys) first; the workgroups of one
+  // (sequence, KV head) are num_seqs * num_kv_heads apart in launch order.
+  const int bid = blockIdx.x;
+  const int g = bid % num_kv_heads;
+  const int rest = bid / num_kv_heads;
+  const int s = rest % num_seqs;
+  const int qt = tiles_per_seq - 1 - rest / num_seqs;
+
+  const int q0 = query_start_loc[s];
+  const int q1 = query_start_loc[s + 1];
+  const int nnew = q1 - q0;
+  const int j0 = qt * kTokens;
+  if (j0 >= nnew) return;
+  const int n = min(context_lens[s], max_context_len);
+  const int first = n - nnew;  // position of new token 0
+  const int jend = min(j0 + kTokens, nnew);
+  const int pmax = first + jend - 1;
+  const int ntiles = pmax >= 0 ? (pmax + kKeys) / kKeys : 0;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int32_t* table = block_tables + (int64_t)s * max_blocks_per_seq;
+
+  // This lane's two rows (one per column tile): token, query head, position.
+  int row_tok[2], row_head[2], pos[2];
+  bool row_ok[2];
+  uint4 qv[2][KK];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int r = wave * kRowsPerWave + 16 * c + col;
+    const int j = j0 + r / G;
+    row_tok[c] = q0 + j;
+    row_head[c] = g * G + r % G;
+    row_ok[c] = j < jend && q0 + j < num_tokens;
+    // rows past the tile's tokens act as its last token (their output is
+    // dropped), so no row is masked everywhere
+    pos[c] = row_ok[c] ? first + j : pmax;
+    const uint16_t* qp = q + ((int64_t)row_tok[c] * num_q_heads + row_head[c]) * D + 8 * grp;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qv[c][kk] = row_ok[c] ? *reinterpret_cast<const uint4*>(qp + 32 * kk) : make_uint4(0, 0, 0, 0);
+  }
+
+  f32x4_t o[2][DT];
+  float m[2], lsum[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    m[c] = -INFINITY;
+    lsum[c] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) o[c][t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  Stage<D> st;
+  if (ntiles > 0) {
+    stage_load<D>(st, k_cache, v_cache, table, 0, n, log2b, g, num_kv_heads, num_blocks);
+    stage_store<D>(st, lds[0][0], lds[0][1]);
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < ntiles)
+      stage_load<D>(st, k_cache, v_cache, table, (kt + 1) * kKeys, n, log2b, g, num_kv_heads,
+                    num_blocks);
+    const uint16_t* lk = lds[buf][0];
+    const uint16_t* lv = lds[buf][1];
+
+    // S^T: keys 16 h + 4 grp + r of the tile, rows col of both column tiles.
+    f32x4_t sc[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      sc[0][h] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      sc[1][h] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const uint4 a = *reinterpret_cast<const uint4*>(lk + (16 * h + col) * Pitch<D>::kElems +
+                                                        32 * kk + 8 * grp);
+        sc[0][h] = mfma16x16x32(a, qv[0][kk], sc[0][h]);
+        sc[1][h] = mfma16x16x32(a, qv[1][kk], sc[1][h]);
+      }
+    }
+
+    // Online softmax of each row; P^T operands (hi and lo parts) in the S^T
+    // key order.
+    uint4 pb[2], pl[2];
+    const int tbase = kt * kKeys + 4 * grp;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float x[2][4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = tbase + 16 * h + r;
+          x[h][r] = t <= pos[c] ? sc[c][h][r] * qscale : -INFINITY;
+          mx = fmaxf(mx, x[h][r]);
+        }
+      mx = rows_max(mx);
+      const bool grow = mx > m[c] + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float alpha = grow ? fast_exp2(m[c] - mx) : 1.0f;
+        if (grow) m[c] = mx;
+        lsum[c] *= alpha;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) o[c][t] *= alpha;
+      }
+      uint32_t ph[4], plo[4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; r += 2) {
+          const float p0 = fast_exp2(x[h][r] - m[c]);
+          const float p1 = fast_exp2(x[h][r + 1] - m[c]);
+          lsum[c] += p0 + p1;
+          const uint32_t h0 = bf16_rne(p0), h1 = bf16_rne(p1);
+          const uint32_t l0 = bf16_rne(p0 - bf16_value(h0)), l1 = bf16_rne(p1 - bf16_value(h1));
+          ph[2 * h + r / 2] = h0 | (h1 << 16);
+          plo[2 * h + r / 2] = l0 | (l1 << 16);
+        }
+      pb[c] = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+      pl[c] = make_uint4(plo[0], plo[1], plo[2], plo[3]);
+    }
+
+    // O^T += V^T P^T.  Transpose reads: within each 16-lane group, lane
+    // 4 k + m names row (key) k at dims d0 + 4 m .. + 3, and lane i receives
+    // dim d0 + i of the 4 keys; the two reads give keys 4 grp + k and
+    // 16 + 4 grp + k, the order of P^T's k-slots.
+    const int key_a = 4 * grp + (col >> 2);
+    const int dofs = 4 * (col & 3);
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)(lv + key_a * Pitch<D>::kElems + 16 * t + dofs));
+      const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)(lv + (key_a + 16) * Pitch<D>::kElems + 16 * t + dofs));
+      uint4 a;
+      a.x = (uint32_t)(uint16_t)v0[0] | ((uint32_t)(uint16_t)v0[1] << 16);
+      a.y = (uint32_t)(uint16_t)v0[2] | ((uint32_t)(uint16_t)v0[3] << 16);
+      a.z = (uint32_t)(uint16_t)v1[0] | ((uint32_t)(uint16_t)v1[1] << 16);
+      a.w = (uint32_t)(uint16_t)v1[2] | ((uint32_t)(uint16_t)v1[3] << 16);
+      o[0][t] = mfma16x16x32(a, pb[0], o[0][t]);
+      o[1][t] = mfma16x16x32(a, pb[1], o[1][t]);
+      o[0][t] = mfma16x16x32(a, pl[0], o[0][t]);
+      o[1][t] = mfma16x16x32(a, pl[1], o[1][t]);
+    }
+
+    if (kt + 1 < ntiles) stage_store<D>(st, lds[buf ^ 1][0], lds[buf ^ 1][1]);
+    __syncthreads();
+  }
+
+  // Normalise and store: lane holds dims 16 t + 4 grp + r of its rows.
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const float l = rows_sum(lsum[c]);
+    if (!row_ok[c]) continue;
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    uint16_t* op = out + ((int64_t)row_tok[c] * num_q_heads + row_head[c]) * D + 4 * grp;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      uint2 w;
+      w.x = bf16_rne(o[c][t][0] * inv) | (bf16_rne(o[c][t][1] * inv) << 16);
+      w.y = bf16_rne(o[c][t][2] * inv) | (bf16_rne(o[c][t][3] * inv) << 16);
+      *reinterpret_cast<uint2*>(op + 16 * t) = w;
+    }
+  }
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+template <int D>
+int launch_d(int G, dim3 grid, hipStream_t st, uint16_t* out, const uint16_t* q,
+             const uint16_t* kc, const uint16_t* vc, const int32_t* bt, int32_t M,
+             const int32_t* ctx, const int32_t* qsl, int32_t S, int32_t T, int32_t hq,
+             int32_t hkv, int32_t nb, int32_t log2b, int32_t maxctx, int32_t tps, float qscale) {
+#define PKV_PREFILL_CASE(GG)                                                                  \
+  case GG:                                                                                    \
+    hipLaunchKernelGGL((prefill_kernel<D, GG>), grid, dim3(kThreads), 0, st, out, q, kc, vc, \
+                       bt, M, ctx, qsl, S, T, hq, hkv, nb, log2b, maxctx, tps, qscale);       \
+    return PKV_OK;
+  switch (G) {
+    PKV_PREFILL_CASE(1)
+    PKV_PREFILL_CASE(2)
+    PKV_PREFILL_CASE(4)
+    PKV_PREFILL_CASE(8)
+    PKV_PREFILL_CASE(16)
+    default:
+      return pkv__fail(PKV_EUNSUPPORTED, "query heads per KV head %d not in {1, 2, 4, 8, 16}", G);
+  }
+#undef PKV_PREFILL_CASE
+}
+
+}  // namespace
+
+extern "C" int pkv_paged_attention_prefill(
+    void* out, const void* q, const void* k_cache, const void* v_cache, const pkv_cache_desc* c,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+    int32_t max_new_tokens, int32_t max_context_len, float scale, void* stream) {
+  pkv__clear_error();
+  int rc = pkv__check_desc(c);
+  if (rc) return rc;
+  if (c->dtype != PKV_BF16)
+    return pkv__fail(PKV_EUNSUPPORTED, "prefill attention is built for bf16 caches only");
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return pkv__fail(PKV_EUNSUPPORTED, "prefill head_dim %d not in {64, 128}", c->head_dim);
+  const int B = c->block_size;
+  if (B != 8 && B != 16 && B != 32)
+    return pkv__fail(PKV_EUNSUPPORTED, "prefill block_size %d not in {8, 16, 32}", B);
+  if (num_seqs < 0 || num_tokens < 0 || max_new_tokens < 0 || max_context_len < 0 ||
+      max_blocks_per_seq < 0)
+    return pkv__fail(PKV_EINVAL, "negative size argument");
+  if (num_q_heads <= 0 || num_q_heads % c->num_kv_heads != 0)
+    return pkv__fail(PKV_EINVAL, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                     num_q_heads, c->num_kv_heads);
+  if (max_new_tokens > num_tokens || max_new_tokens > max_context_len)
+    return pkv__fail(PKV_EINVAL, "max_new_tokens %d exceeds num_tokens %d or max_context_len %d",
+                     max_new_tokens, num_tokens, max_context_len);
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * B)
+    return pkv__fail(PKV_EINVAL, "max_context_len %d exceeds the table width %d x block_size %d",
+                     max_context_len, max_blocks_per_seq, B);
+  if (num_seqs == 0 || num_tokens == 0 || max_new_tokens == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc)
+    return pkv__fail(PKV_EINVAL, "NULL device pointer");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      ((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u) ||
+      ((uintptr_t)query_start_loc & 3u))
+    return pkv__fail(PKV_EINVAL, "q, out and the caches must be 16-byte aligned, index arrays 4-byte");
+  const int G = num_q_heads / c->num_kv_heads;
+  if (G > kRowsPerGroup || kRowsPerGroup % G != 0)
+    return pkv__fail(PKV_EUNSUPPORTED, "query heads per KV head %d not in {1, 2, 4, 8, 16}", G);
+  const int64_t tokens_per_group = kRowsPerGroup / G;
+  const int64_t tps = (max_new_tokens + tokens_per_group - 1) / tokens_per_group;
+  const int64_t grid = tps * num_seqs * c->num_kv_heads;
+  if (grid > INT32_MAX) return pkv__fail(PKV_EINVAL, "prefill grid too large");
+  const int log2b = B == 8 ? 3 : (B == 16 ? 4 : 5);
+  const float qscale = scale * 1.4426950408889634f;  // logits in log2 units
+  hipStream_t st = (hipStream_t)stream;
+  if (c->head_dim == 128)
+    rc = launch_d<128>(G, dim3((uint32_t)grid), st, (uint16_t*)out, (const uint16_t*)q,
+                       (const uint16_t*)k_cache, (const uint16_t*)v_cache, block_tables,
+                       max_blocks_per_seq, context_lens, query_start_loc, num_seqs, num_tokens,
+                       num_q_heads, c->num_kv_heads, c->num_blocks, log2b, max_context_len,
+                       (int32_t)tps, qscale);
+  else
+    rc = launch_d<64>(G, dim3((uint32_t)grid), st, (uint16_t*)out, (const uint16_t*)q,
+                      (const uint16_t*)k_cache, (const uint16_t*)v_cache, block_tables,
+                      max_blocks_per_seq, context_lens, query_start_loc, num_seqs, num_tokens,
+                      num_q_heads, c->num_kv_heads, c->num_blocks, log2b, max_context_len,
+                      (int32_t)tps, qscale);
+  if (rc) return rc;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return pkv__fail(PKV_EHIP, "prefill launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}

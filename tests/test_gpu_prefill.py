@@ -1,0 +1,168 @@
+"""GPU parity of causal paged prefill attention against the fp64 oracle.
+
+Pools are filled with seeded N(0, 1) bf16 values, tables come from the
+oracle's allocator with a seeded free order, and every slot no sequence reads
+holds NaN.  Small cases (several query and key tiles, ragged tails, every
+built group size and head_dim, block sizes 8/16/32) compare every output
+element; the full-size chunked-prefill workload compares sampled sequences
+in the launch the benchmark times."""
+
+import math
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import datagen  # noqa: E402
+import paged_kv_cache_377_amd as pkv  # noqa: E402
+from datagen import normal, poison_unused  # noqa: E402
+from oracle import BlockAllocatorModel, paged_attention_decode, paged_attention_prefill  # noqa: E402
+from tests.gpu_util import check_close, dev, host  # noqa: E402
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _case(rng, lens, news, hq, hkv, D, B, extra_blocks=5, poison=True):
+    ctx = np.array(lens, np.int32)
+    need = sum(-(-int(n) // B) for n in ctx)
+    nb = need + extra_blocks
+    order = rng.permutation(nb).astype(np.int32)
+    m = BlockAllocatorModel(nb, B, order)
+    for s, n in enumerate(ctx):
+        m.add(s, int(n))
+    width = max(1, max(-(-int(n) // B) for n in ctx))
+    t, _ = m.build_tables(list(range(len(ctx))), width)
+    tables = np.array(t, np.int32)
+    kc = normal(rng, (nb, hkv, B, D), "bf16")
+    vc = normal(rng, (nb, hkv, B, D), "bf16")
+    if poison:
+        poison_unused(kc, vc, tables, ctx, B, "bf16")
+    qsl = np.concatenate([[0], np.cumsum(news)]).astype(np.int32)
+    q = normal(rng, (int(qsl[-1]), hq, D), "bf16")
+    return q, kc, vc, tables, ctx, qsl
+
+
+def _run(q, kc, vc, tables, ctx, qsl, scale, dkc=None, dvc=None):
+    dq = dev(q)
+    out = torch.full_like(dq, float("nan"))
+    news = np.diff(qsl)
+    pkv.paged_attention_prefill(out, dq, dev(kc) if dkc is None else dkc,
+                                dev(vc) if dvc is None else dvc, dev(tables), dev(ctx), dev(qsl),
+                                scale, int(news.max()) if len(news) else 0,
+                                int(ctx.max()) if len(ctx) else 0)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+SMALL = [  # (lens, new tokens, hq, hkv, D, B)
+    ([40, 100, 7, 300], [40, 33, 7, 129], 32, 8, 128, 16),      # G 4: fresh, partial, tiny, 2 q-tiles
+    ([300, 129, 5], [300, 1, 5], 8, 8, 64, 8),                   # G 1, 128 tokens per workgroup
+    ([64, 200], [64, 150], 16, 2, 128, 32),                      # G 8
+    ([97, 33], [97, 20], 4, 2, 64, 16),                          # G 2
+    ([70, 18], [70, 17], 32, 2, 128, 16),                        # G 16: 8 tokens per workgroup
+    ([50, 0, 31], [0, 0, 31], 8, 2, 128, 16),                    # no new tokens, empty sequence
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"c{i}" for i in range(len(SMALL))])
+def test_small_cases_every_element(case):
+    lens, news, hq, hkv, D, B = case
+    print(f"prefill small {case}", flush=True)
+    rng = np.random.default_rng(sum(lens) + 7 * hq + D + B)
+    q, kc, vc, tables, ctx, qsl = _case(rng, lens, news, hq, hkv, D, B)
+    scale = 1.0 / math.sqrt(D)
+    got = _run(q, kc, vc, tables, ctx, qsl, scale)
+    ref = paged_attention_prefill(q, kc, vc, tables, ctx, qsl, scale, "bf16")
+    print("max_abs/max_rel", check_close(got, ref, "bf16"))
+
+
+def test_one_new_token_per_sequence_matches_decode():
+    rng = np.random.default_rng(41)
+    lens = [1, 15, 16, 17, 200, 1000]
+    q, kc, vc, tables, ctx, qsl = _case(rng, lens, [1] * len(lens), 32, 8, 128, 16)
+    got = _run(q, kc, vc, tables, ctx, qsl, 0.1)
+    ref = paged_attention_decode(q, kc, vc, tables, ctx, 0.1, "bf16")
+    check_close(got, ref, "bf16")
+
+
+def test_chunked_prefill_through_the_table():
+    """A prompt prefilled in three chunks: each chunk's call sees the earlier
+    chunks only through the table, and matches the oracle's rows of one
+    prefill of the whole prompt."""
+    rng = np.random.default_rng(42)
+    n, D = 700, 128
+    q, kc, vc, tables, ctx, _ = _case(rng, [n], [n], 32, 8, D, 16)
+    scale = 1.0 / math.sqrt(D)
+    whole = paged_attention_prefill(q, kc, vc, tables, ctx, np.array([0, n], np.int32), scale, "bf16")
+    dkc, dvc = dev(kc), dev(vc)
+    for a, b in [(0, 128), (128, 300), (300, n)]:
+        got = _run(q[a:b], kc, vc, tables, np.array([b], np.int32), np.array([0, b - a], np.int32),
+                   scale, dkc, dvc)
+        check_close(got, whole[a:b], "bf16")
+
+
+def test_poison_permutation_and_determinism():
+    rng = np.random.default_rng(43)
+    lens, news = [260, 45, 513], [100, 45, 3]
+    q, kc, vc, tables, ctx, qsl = _case(rng, lens, news, 32, 8, 128, 16, extra_blocks=9)
+    a = _run(q, kc, vc, tables, ctx, qsl, 0.09)
+    b = _run(q, kc, vc, tables, ctx, qsl, 0.09)
+    assert np.array_equal(a, b), "two runs differ"
+    perm = rng.permutation(kc.shape[0])
+    inv = np.argsort(perm).astype(np.int32)
+    c = _run(q, kc[perm], vc[perm], inv[tables], ctx, qsl, 0.09)
+    assert np.array_equal(a, c), "physical block ids leak into the result"
+    kc2, vc2 = kc.copy(), vc.copy()
+    kc2[:] = datagen.nan_bits("bf16")
+    vc2[:] = datagen.nan_bits("bf16")
+    live = np.zeros(kc.shape[0], bool)
+    for t, n in zip(tables, ctx):
+        live[t[: -(-int(n) // 16)]] = True
+    kc2[live], vc2[live] = kc[live], vc[live]
+    d = _run(q, kc2, vc2, tables, ctx, qsl, 0.09)
+    assert np.array_equal(a, d), "unread blocks reach the result"
+
+
+def test_rejects_unbuilt_shapes_and_bad_bounds():
+    q = torch.zeros((4, 8, 128), dtype=torch.float32, device="cuda")
+    kc = torch.zeros((4, 2, 16, 128), dtype=torch.float32, device="cuda")
+    t = torch.zeros((1, 4), dtype=torch.int32, device="cuda")
+    ctx = torch.tensor([4], dtype=torch.int32, device="cuda")
+    qsl = torch.tensor([0, 4], dtype=torch.int32, device="cuda")
+    with pytest.raises(pkv.PagedKVError) as ei:
+        pkv.paged_attention_prefill(q.clone(), q, kc, kc, t, ctx, qsl, 1.0, 4, 4)
+    assert ei.value.code == pkv.PKV_EUNSUPPORTED
+    qb, kb = q.bfloat16(), kc.bfloat16()
+    with pytest.raises(pkv.PagedKVError) as ei:
+        pkv.paged_attention_prefill(qb.clone(), qb, kb, kb, t, ctx, qsl, 1.0, 4, 65)
+    assert ei.value.code == pkv.PKV_EINVAL   # max_context_len beyond the table width
+
+
+def test_chunked_prefill_workload_full_size():
+    """16 sequences, each a cached prefix of U{0..2048} tokens plus a 512-token
+    chunk, Llama-3-8B layer shape: sampled sequences, every head and row."""
+    w = datagen.prefill_inputs()
+    sh = w.shape
+    S, B = sh.num_seqs, sh.block_size
+    print(f"prefill full size: S={S} T={int(w.qsl[-1])} pool={w.num_blocks}", flush=True)
+    m = BlockAllocatorModel(w.num_blocks, B, w.free_order)
+    for s, n in enumerate(w.context_lens):
+        m.add(s, int(n))
+    t, _ = m.build_tables(list(range(S)), max(-(-int(n) // B) for n in w.context_lens))
+    tables = np.array(t, np.int32)
+    poison_unused(w.k_cache, w.v_cache, tables, w.context_lens, B, sh.dtype)
+    got = _run(w.q, w.k_cache, w.v_cache, tables, w.context_lens, w.qsl, sh.scale)
+    rng = np.random.default_rng(44)
+    sample = sorted({0, S - 1, int(np.argmax(w.context_lens))} |
+                    set(rng.choice(S, 1, replace=False).tolist()))
+    ref = paged_attention_prefill(w.q, w.k_cache, w.v_cache, tables, w.context_lens, w.qsl,
+                                  sh.scale, "bf16", seqs=sample)
+    rows = np.concatenate([np.arange(w.qsl[s], w.qsl[s + 1]) for s in sample])
+    print("prefill full max_abs/max_rel", check_close(got[rows], ref[rows], "bf16"))
