@@ -20,6 +20,9 @@ Workloads (seeded synthetic inputs, see datagen):
   6  prefix caching: 64 requests = one 1024-token system prompt + their own
      U{16..1024}-token question, admitted by token ids through the
      allocator's prefix cache (host admission cost and hit rate reported)
+  7  chunked prefill: 16 seqs = cached prefix U{0..2048} + a 512-token chunk;
+     a step writes the chunk's K/V and runs the causal prefill attention;
+     reported in attention TFLOP/s against the bf16 MFMA peak
 
 Prints one JSON line.  ``value`` = algorithmic KV bytes the decode reads per
 step / step time, in GB/s (1e9 B/s).  ``roofline`` reports the decode call
@@ -39,6 +42,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 WORKLOAD_NAMES = {
@@ -52,6 +56,8 @@ WORKLOAD_NAMES = {
        "head_dim 128, bf16",
     6: "prefix-cached decode: 64 requests = shared 1024-token system prompt + U{16..1024}-token "
        "question, 32 q / 8 kv heads, head_dim 128, bf16, block 16",
+    7: "chunked prefill: 16 seqs = cached prefix U{0..2048} + 512 new tokens, 32 q / 8 kv heads, "
+       "head_dim 128, bf16, block 16",
 }
 
 
@@ -60,7 +66,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6])
+    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6, 7])
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--partition-size", type=int, default=-1,
                     help="-1: balanced split (default); > 0: split-context partitions; 0: no split")
@@ -348,6 +354,121 @@ def copy_probe(mib: int, reps: int) -> None:
           flush=True)
 
 
+def prefill_flops(ctx, qsl, num_q_heads: int, head_dim: int) -> int:
+    """Attention flops of a causal prefill: 4 D per (query row, head, key it
+    sees) -- 2 D for the logit, 2 D for the weighted value."""
+    pairs = 0
+    for n, a, b in zip(ctx, qsl[:-1], qsl[1:]):
+        m = int(b) - int(a)
+        first = int(n) - m
+        pairs += m * first + m * (m + 1) // 2
+    return 4 * head_dim * num_q_heads * pairs
+
+
+def run_prefill(args, torch, pkv):
+    import datagen
+
+    w = datagen.prefill_inputs(block_size=args.block_size or 16)
+    sh = w.shape
+    S, B = sh.num_seqs, sh.block_size
+    chunk = int(w.qsl[1] - w.qsl[0])
+    alloc = pkv.BlockAllocator(w.num_blocks, B, w.free_order)
+    slots = []
+    for s_ in range(S):
+        sl = alloc.add(s_, int(w.context_lens[s_]))
+        slots.append(sl[-chunk:])       # the chunk's own positions
+    seq_ids = np.arange(S, dtype=np.int64)
+    width = max(-(-int(n) // B) for n in w.context_lens)
+    tables, ctx = alloc.build_tables(seq_ids, width)
+    rng = np.random.default_rng(datagen.seed_for(7) + 31)
+    T = S * chunk
+    nk = datagen.normal(rng, (T, sh.num_kv_heads, sh.head_dim), sh.dtype)
+    nv = datagen.normal(rng, (T, sh.num_kv_heads, sh.head_dim), sh.dtype)
+    kc, vc = to_dev(w.k_cache, torch), to_dev(w.v_cache, torch)
+    d = dict(q=to_dev(w.q, torch), k=to_dev(nk, torch), v=to_dev(nv, torch),
+             slots=to_dev(np.concatenate(slots), torch), tables=to_dev(tables, torch),
+             ctx=to_dev(ctx, torch), qsl=to_dev(w.qsl, torch))
+    out = torch.empty_like(d["q"])
+    stream = torch.cuda.current_stream()
+    max_ctx = int(ctx.max())
+
+    def attn():
+        pkv.paged_attention_prefill(out, d["q"], kc, vc, d["tables"], d["ctx"], d["qsl"], sh.scale,
+                                    chunk, max_ctx, stream=stream)
+
+    def step():
+        pkv.paged_kv_write(d["k"], d["v"], d["slots"], kc, vc, stream=stream)
+        attn()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev2, ev3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev2.record(stream)
+    for _ in range(args.steps):
+        attn()
+    ev3.record(stream)
+    torch.cuda.synchronize()
+    attn_ms = ev2.elapsed_time(ev3) / args.steps
+    flops = prefill_flops(ctx, w.qsl, sh.num_q_heads, sh.head_dim)
+    ms_per_step = wall * 1e3 / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    res = {
+        "metric": "paged-prefill attention TFLOP/s", "value": round(value, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/K/V, allocator-scattered blocks)",
+        "config": {"workload": WORKLOAD_NAMES[7], "num_seqs": S, "new_tokens": T,
+                   "num_q_heads": sh.num_q_heads, "num_kv_heads": sh.num_kv_heads,
+                   "head_dim": sh.head_dim, "block_size": B, "pool_blocks": w.num_blocks,
+                   "mean_context": float(ctx.mean())},
+        "attn_ms": round(attn_ms, 4),
+        "tokens_per_s": round(T / (attn_ms * 1e-3), 1),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "paged_attention_prefill",
+                     "algorithmic_flops_per_launch": int(flops)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(w, tables, ctx)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_prefill(w, tables, ctx, min_s: float = 10.0):
+    """fp64 oracle prefill on one host core, one sequence at a time (all its
+    heads and rows) until ``min_s`` seconds; TFLOP/s over the same count."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    sh = w.shape
+    done, flops = [], 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        for s_ in range(sh.num_seqs):
+            oracle.paged_attention_prefill(w.q, w.k_cache, w.v_cache, tables, ctx, w.qsl, sh.scale,
+                                           sh.dtype, seqs=[s_])
+            done.append(s_)
+            flops += prefill_flops(ctx[s_:s_ + 1], w.qsl[s_:s_ + 2] - w.qsl[s_], sh.num_q_heads,
+                                   sh.head_dim)
+            if time.perf_counter() - t0 >= min_s:
+                break
+    el = time.perf_counter() - t0
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 prefill of {len(done)} of {sh.num_seqs} sequences (all rows and heads) "
+                      f"in {el:.1f} s, numpy/BLAS limited to 1 thread"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -362,6 +483,9 @@ def main():
         sys.exit(1)
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib, max(args.steps, 1))
+        return
+    if args.workload == 7:
+        run_prefill(args, torch, pkv)
         return
     total = args.warmup + args.steps
     t_setup = time.perf_counter()

@@ -71,13 +71,14 @@ __device__ inline f32x4_t mfma16x16x32(const uint4& a, const uint4& b, const f32
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
-__device__ inline uint32_t bf16_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-__device__ inline float bf16_value(uint32_t b) { return __uint_as_float(b << 16); }
+// Two fp32 -> packed bf16 pair (lo in bits 0..15), round to nearest even
+// (one v_cvt_pk_bf16_f32).
+__device__ inline uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
 
 // Max / sum over the four 16-lane groups of the wave (lanes with equal
 // l % 16), with the VALU row-swap instructions.
@@ -104,51 +105,85 @@ struct Pitch {
   static constexpr int kTile = kKeys * kElems;  // elements per staged matrix
 };
 
-// One thread's share of staging a K/V tile: D / 64 pieces of 16 bytes of K
-// and the same of V (a tile is 32 rows of D bf16 = 4 D pieces per matrix).
+// One thread's share of staging a K/V tile: D / 64 (1 or 2) pieces of 16
+// bytes of K and the same of V (a tile is 32 rows of D bf16 = 4 D pieces per
+// matrix), and whether each piece's row is live.  Plain members, no arrays:
+// the compiler keeps them in registers.  Every load is issued unconditionally
+// -- a row that is not live (past the context, or whose block id lies outside
+// the pool) reads the first piece of the pool instead and is stored as zeros
+// -- so the loads stay in flight across the MFMA work instead of being waited
+// for at a branch.
 template <int D>
 struct Stage {
   static constexpr int kPer = D / 64;
-  uint4 k[kPer], v[kPer];
+  static constexpr int kChunks = D / 8;  // 16-byte pieces per key row
+  uint4 k0, v0, k1, v1;
+  bool ok0, ok1;
+  int e0, e1;  // table entries of the next tile to load
 };
+
+__device__ inline int stage_key(int u, int chunks) { return (threadIdx.x + kThreads * u) / chunks; }
+
+// Table entries of this thread's rows of key tile `t0` (positions clamped to
+// the context, so every read is inside the sequence's row of the table).
+template <int D>
+__device__ inline void stage_entries(Stage<D>& st, const int32_t* __restrict__ table, int t0,
+                                     int n, int log2b) {
+  st.e0 = table[min(t0 + stage_key(0, Stage<D>::kChunks), n - 1) >> log2b];
+  if constexpr (Stage<D>::kPer == 2)
+    st.e1 = table[min(t0 + stage_key(1, Stage<D>::kChunks), n - 1) >> log2b];
+}
+
+template <int D>
+__device__ inline void stage_piece(uint4& k, uint4& v, bool& ok, int e, int u,
+                                   const uint16_t* __restrict__ k_cache,
+                                   const uint16_t* __restrict__ v_cache, int t0, int n, int log2b,
+                                   int g, int num_kv_heads, int num_blocks) {
+  const int idx = threadIdx.x + kThreads * u;
+  const int key = idx / Stage<D>::kChunks;
+  const int c = idx - key * Stage<D>::kChunks;
+  const int t = t0 + key;
+  ok = (t < n) & (e >= 0) & (e < num_blocks);
+  const int64_t row = ((int64_t)e * num_kv_heads + g) * ((int64_t)1 << log2b) + (t & ((1 << log2b) - 1));
+  const int64_t off = ok ? row * D + 8 * c : 0;
+  k = *reinterpret_cast<const uint4*>(k_cache + off);
+  v = *reinterpret_cast<const uint4*>(v_cache + off);
+}
 
 template <int D>
 __device__ inline void stage_load(Stage<D>& st, const uint16_t* __restrict__ k_cache,
-                                  const uint16_t* __restrict__ v_cache,
-                                  const int32_t* __restrict__ table, int t0, int n, int log2b,
+                                  const uint16_t* __restrict__ v_cache, int t0, int n, int log2b,
                                   int g, int num_kv_heads, int num_blocks) {
-  constexpr int kChunks = D / 8;  // 16-byte pieces per key row
-#pragma unroll
-  for (int u = 0; u < Stage<D>::kPer; ++u) {
-    const int idx = threadIdx.x + kThreads * u;
-    const int key = idx / kChunks;
-    const int c = idx - key * kChunks;
-    const int t = t0 + key;
-    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-    if (t < n) {
-      const int phys = table[t >> log2b];
-      if (phys >= 0 && phys < num_blocks) {
-        const int64_t row = ((int64_t)phys * num_kv_heads + g) * ((int64_t)1 << log2b) +
-                            (t & ((1 << log2b) - 1));
-        kv = *reinterpret_cast<const uint4*>(k_cache + row * D + 8 * c);
-        vv = *reinterpret_cast<const uint4*>(v_cache + row * D + 8 * c);
-      }
-    }
-    st.k[u] = kv;
-    st.v[u] = vv;
-  }
+  stage_piece<D>(st.k0, st.v0, st.ok0, st.e0, 0, k_cache, v_cache, t0, n, log2b, g, num_kv_heads,
+                 num_blocks);
+  if constexpr (Stage<D>::kPer == 2)
+    stage_piece<D>(st.k1, st.v1, st.ok1, st.e1, 1, k_cache, v_cache, t0, n, log2b, g,
+                   num_kv_heads, num_blocks);
+}
+
+// x if keep, else zeros: a mask on each 32-bit part (a select of whole
+// vectors can turn into a select of their addresses, which sends the staging
+// registers to scratch memory).
+__device__ inline uint4 keep_or_zero(uint4 x, bool keep) {
+  const uint32_t m = keep ? 0xffffffffu : 0u;
+  return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
 }
 
 template <int D>
 __device__ inline void stage_store(const Stage<D>& st, uint16_t* lk, uint16_t* lv) {
-  constexpr int kChunks = D / 8;
-#pragma unroll
-  for (int u = 0; u < Stage<D>::kPer; ++u) {
-    const int idx = threadIdx.x + kThreads * u;
-    const int key = idx / kChunks;
-    const int c = idx - key * kChunks;
-    *reinterpret_cast<uint4*>(lk + key * Pitch<D>::kElems + 8 * c) = st.k[u];
-    *reinterpret_cast<uint4*>(lv + key * Pitch<D>::kElems + 8 * c) = st.v[u];
+  {
+    const int idx = threadIdx.x;
+    const int key = idx / Stage<D>::kChunks;
+    const int c = idx - key * Stage<D>::kChunks;
+    *reinterpret_cast<uint4*>(lk + key * Pitch<D>::kElems + 8 * c) = keep_or_zero(st.k0, st.ok0);
+    *reinterpret_cast<uint4*>(lv + key * Pitch<D>::kElems + 8 * c) = keep_or_zero(st.v0, st.ok0);
+  }
+  if constexpr (Stage<D>::kPer == 2) {
+    const int idx = threadIdx.x + kThreads;
+    const int key = idx / Stage<D>::kChunks;
+    const int c = idx - key * Stage<D>::kChunks;
+    *reinterpret_cast<uint4*>(lk + key * Pitch<D>::kElems + 8 * c) = keep_or_zero(st.k1, st.ok1);
+    *reinterpret_cast<uint4*>(lv + key * Pitch<D>::kElems + 8 * c) = keep_or_zero(st.v1, st.ok1);
   }
 }
 
@@ -222,18 +257,22 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     for (int t = 0; t < DT; ++t) o[c][t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
+  // Pipeline: table entries two tiles ahead, K/V one tile ahead (registers),
+  // the current tile in LDS.  The loads past the last tile read live memory
+  // and land in the unused buffer.
   Stage<D> st;
   if (ntiles > 0) {
-    stage_load<D>(st, k_cache, v_cache, table, 0, n, log2b, g, num_kv_heads, num_blocks);
+    stage_entries<D>(st, table, 0, n, log2b);
+    stage_load<D>(st, k_cache, v_cache, 0, n, log2b, g, num_kv_heads, num_blocks);
+    stage_entries<D>(st, table, kKeys, n, log2b);
     stage_store<D>(st, lds[0][0], lds[0][1]);
   }
   __syncthreads();
 
   for (int kt = 0; kt < ntiles; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < ntiles)
-      stage_load<D>(st, k_cache, v_cache, table, (kt + 1) * kKeys, n, log2b, g, num_kv_heads,
-                    num_blocks);
+    stage_load<D>(st, k_cache, v_cache, (kt + 1) * kKeys, n, log2b, g, num_kv_heads, num_blocks);
+    stage_entries<D>(st, table, (kt + 2) * kKeys, n, log2b);
     const uint16_t* lk = lds[buf][0];
     const uint16_t* lv = lds[buf][1];
 
@@ -253,9 +292,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     }
 
     // Online softmax of each row; P^T operands (hi and lo parts) in the S^T
-    // key order.
+    // key order.  Only tiles that reach past the workgroup's first position
+    // need the causal mask (wave-uniform test).
     uint4 pb[2], pl[2];
     const int tbase = kt * kKeys + 4 * grp;
+    const bool masked = (kt + 1) * kKeys - 1 > first + j0;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       float x[2][4];
@@ -265,7 +306,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = tbase + 16 * h + r;
-          x[h][r] = t <= pos[c] ? sc[c][h][r] * qscale : -INFINITY;
+          x[h][r] = sc[c][h][r] * qscale;
+          if (masked) x[h][r] = t <= pos[c] ? x[h][r] : -INFINITY;
           mx = fmaxf(mx, x[h][r]);
         }
       mx = rows_max(mx);
@@ -285,10 +327,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
           const float p0 = fast_exp2(x[h][r] - m[c]);
           const float p1 = fast_exp2(x[h][r + 1] - m[c]);
           lsum[c] += p0 + p1;
-          const uint32_t h0 = bf16_rne(p0), h1 = bf16_rne(p1);
-          const uint32_t l0 = bf16_rne(p0 - bf16_value(h0)), l1 = bf16_rne(p1 - bf16_value(h1));
-          ph[2 * h + r / 2] = h0 | (h1 << 16);
-          plo[2 * h + r / 2] = l0 | (l1 << 16);
+          const uint32_t hp = pack_bf16(p0, p1);
+          ph[2 * h + r / 2] = hp;
+          plo[2 * h + r / 2] = pack_bf16(p0 - __uint_as_float(hp << 16),
+                                         p1 - __uint_as_float(hp & 0xffff0000u));
         }
       pb[c] = make_uint4(ph[0], ph[1], ph[2], ph[3]);
       pl[c] = make_uint4(plo[0], plo[1], plo[2], plo[3]);
@@ -306,18 +348,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
           (lds_s16x4_t*)(lv + key_a * Pitch<D>::kElems + 16 * t + dofs));
       const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4_t*)(lv + (key_a + 16) * Pitch<D>::kElems + 16 * t + dofs));
-      uint4 a;
-      a.x = (uint32_t)(uint16_t)v0[0] | ((uint32_t)(uint16_t)v0[1] << 16);
-      a.y = (uint32_t)(uint16_t)v0[2] | ((uint32_t)(uint16_t)v0[3] << 16);
-      a.z = (uint32_t)(uint16_t)v1[0] | ((uint32_t)(uint16_t)v1[1] << 16);
-      a.w = (uint32_t)(uint16_t)v1[2] | ((uint32_t)(uint16_t)v1[3] << 16);
+      const uint2 a0 = __builtin_bit_cast(uint2, v0);
+      const uint2 a1 = __builtin_bit_cast(uint2, v1);
+      const uint4 a = make_uint4(a0.x, a0.y, a1.x, a1.y);
       o[0][t] = mfma16x16x32(a, pb[0], o[0][t]);
       o[1][t] = mfma16x16x32(a, pb[1], o[1][t]);
       o[0][t] = mfma16x16x32(a, pl[0], o[0][t]);
       o[1][t] = mfma16x16x32(a, pl[1], o[1][t]);
     }
 
-    if (kt + 1 < ntiles) stage_store<D>(st, lds[buf ^ 1][0], lds[buf ^ 1][1]);
+    stage_store<D>(st, lds[buf ^ 1][0], lds[buf ^ 1][1]);
     __syncthreads();
   }
 
@@ -331,8 +371,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
       uint2 w;
-      w.x = bf16_rne(o[c][t][0] * inv) | (bf16_rne(o[c][t][1] * inv) << 16);
-      w.y = bf16_rne(o[c][t][2] * inv) | (bf16_rne(o[c][t][3] * inv) << 16);
+      w.x = pack_bf16(o[c][t][0] * inv, o[c][t][1] * inv);
+      w.y = pack_bf16(o[c][t][2] * inv, o[c][t][3] * inv);
       *reinterpret_cast<uint2*>(op + 16 * t) = w;
     }
   }
