@@ -190,6 +190,7 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
  *                    at most num_tokens
  *   max_new_tokens   host int, >= every n_new (sizes the launch)
  *   max_context_len  host int, >= every context_lens[s]
+ *   scale            finite and > 0 (PKV_EINVAL otherwise)
  * Positions after a row's own never affect it; slots at positions >= n and
  * blocks the table does not reach are never used.  Bad device-side contents
  * (n_new > n, table entries outside the pool) never lead to an access

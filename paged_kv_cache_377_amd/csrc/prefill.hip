@@ -117,6 +117,7 @@ template <int D>
 struct Stage {
   static constexpr int kPer = D / 64;
   static constexpr int kChunks = D / 8;  // 16-byte pieces per key row
+  static constexpr int kLog2D = D == 128 ? 7 : 6;
   uint4 k0, v0, k1, v1;
   bool ok0, ok1;
   int e0, e1;  // table entries of the next tile to load
@@ -144,10 +145,14 @@ __device__ inline void stage_piece(uint4& k, uint4& v, bool& ok, int e, int u,
   const int c = idx - key * Stage<D>::kChunks;
   const int t = t0 + key;
   ok = (t < n) & (e >= 0) & (e < num_blocks);
-  const int64_t row = ((int64_t)e * num_kv_heads + g) * ((int64_t)1 << log2b) + (t & ((1 << log2b) - 1));
-  const int64_t off = ok ? row * D + 8 * c : 0;
-  k = *reinterpret_cast<const uint4*>(k_cache + off);
-  v = *reinterpret_cast<const uint4*>(v_cache + off);
+  // (block, head) run index fits 32 bits (num_blocks * num_kv_heads < 2^31,
+  // checked by the host); one 64-bit shift-add gives the element offset
+  const int run = e * num_kv_heads + g;
+  const int64_t off = ((int64_t)run << (log2b + Stage<D>::kLog2D)) +
+                      (((t & ((1 << log2b) - 1)) * D) + 8 * c);
+  const int64_t at = ok ? off : 0;
+  k = *reinterpret_cast<const uint4*>(k_cache + at);
+  v = *reinterpret_cast<const uint4*>(v_cache + at);
 }
 
 template <int D>
@@ -163,7 +168,10 @@ __device__ inline void stage_load(Stage<D>& st, const uint16_t* __restrict__ k_c
 
 // x if keep, else zeros: a mask on each 32-bit part (a select of whole
 // vectors can turn into a select of their addresses, which sends the staging
-// registers to scratch memory).
+// registers to scratch memory).  Only V rows need it: a K row that is not
+// live only meets logits the causal mask replaces by -inf (such rows lie past
+// every row's position), while its V row is multiplied by weight 0, which
+// must not meet NaN or Inf.
 __device__ inline uint4 keep_or_zero(uint4 x, bool keep) {
   const uint32_t m = keep ? 0xffffffffu : 0u;
   return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
@@ -175,14 +183,14 @@ __device__ inline void stage_store(const Stage<D>& st, uint16_t* lk, uint16_t* l
     const int idx = threadIdx.x;
     const int key = idx / Stage<D>::kChunks;
     const int c = idx - key * Stage<D>::kChunks;
-    *reinterpret_cast<uint4*>(lk + key * Pitch<D>::kElems + 8 * c) = keep_or_zero(st.k0, st.ok0);
+    *reinterpret_cast<uint4*>(lk + key * Pitch<D>::kElems + 8 * c) = st.k0;
     *reinterpret_cast<uint4*>(lv + key * Pitch<D>::kElems + 8 * c) = keep_or_zero(st.v0, st.ok0);
   }
   if constexpr (Stage<D>::kPer == 2) {
     const int idx = threadIdx.x + kThreads;
     const int key = idx / Stage<D>::kChunks;
     const int c = idx - key * Stage<D>::kChunks;
-    *reinterpret_cast<uint4*>(lk + key * Pitch<D>::kElems + 8 * c) = keep_or_zero(st.k1, st.ok1);
+    *reinterpret_cast<uint4*>(lk + key * Pitch<D>::kElems + 8 * c) = st.k1;
     *reinterpret_cast<uint4*>(lv + key * Pitch<D>::kElems + 8 * c) = keep_or_zero(st.v1, st.ok1);
   }
 }
@@ -299,6 +307,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const bool masked = (kt + 1) * kKeys - 1 > first + j0;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
+      // raw logits; qscale > 0, so the scaled maximum is qscale * max
       float x[2][4];
       float mx = -INFINITY;
 #pragma unroll
@@ -306,11 +315,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = tbase + 16 * h + r;
-          x[h][r] = sc[c][h][r] * qscale;
+          x[h][r] = sc[c][h][r];
           if (masked) x[h][r] = t <= pos[c] ? x[h][r] : -INFINITY;
           mx = fmaxf(mx, x[h][r]);
         }
-      mx = rows_max(mx);
+      mx = rows_max(mx) * qscale;
       const bool grow = mx > m[c] + kRescaleSlack;
       if (__builtin_amdgcn_ballot_w64(grow)) {
         const float alpha = grow ? fast_exp2(m[c] - mx) : 1.0f;
@@ -324,8 +333,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int r = 0; r < 4; r += 2) {
-          const float p0 = fast_exp2(x[h][r] - m[c]);
-          const float p1 = fast_exp2(x[h][r + 1] - m[c]);
+          const float p0 = fast_exp2(fmaf(x[h][r], qscale, -m[c]));
+          const float p1 = fast_exp2(fmaf(x[h][r + 1], qscale, -m[c]));
           lsum[c] += p0 + p1;
           const uint32_t hp = pack_bf16(p0, p1);
           ph[2 * h + r / 2] = hp;
@@ -431,6 +440,10 @@ extern "C" int pkv_paged_attention_prefill(
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * B)
     return pkv__fail(PKV_EINVAL, "max_context_len %d exceeds the table width %d x block_size %d",
                      max_context_len, max_blocks_per_seq, B);
+  if (!(scale > 0.0f) || scale == INFINITY)
+    return pkv__fail(PKV_EINVAL, "prefill scale must be finite and positive");
+  if ((int64_t)c->num_blocks * c->num_kv_heads > INT32_MAX)
+    return pkv__fail(PKV_EUNSUPPORTED, "num_blocks * num_kv_heads exceeds 2^31 - 1");
   if (num_seqs == 0 || num_tokens == 0 || max_new_tokens == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc)
     return pkv__fail(PKV_EINVAL, "NULL device pointer");
