@@ -73,6 +73,21 @@ Readings taken where the pages are silent:
   entered.  A fork copies the parent's history.
 * Cache statistics count every full prompt block looked up (a query) and
   every block found (a hit); the hit rate is hits / queries.
+
+Swapping (optional host pool; page 3, section 02, the OS-to-vLLM table, row
+"swap to disk": blocks of preempted requests move to host memory and back):
+
+* A group of sequences moves as a whole.  Every block they map is copied
+  once (first appearance in array order, then table order) to a host block
+  taken from the host free list's head; the copy pairs are returned in that
+  order, the host block inherits the device block's count, and the device
+  blocks are then released last pair first (as a finished sequence releases
+  its blocks).  Swapping in is the mirror image.
+* Readings: a block the group shares with a sequence outside it cannot move
+  (E_INVAL); a swap is all-or-nothing (E_NOBLOCKS when the target pool holds
+  fewer free blocks than the group's distinct blocks); a swapped-out
+  sequence cannot append, fork or be tabled until it is swapped back in, but
+  it can be freed (its host blocks go to the host free list's tail).
 """
 
 from __future__ import annotations
@@ -120,6 +135,10 @@ class BlockAllocatorModel:
         self.hits = 0
         self.queries = 0
         self.evictions = 0
+        # host pool for swapped-out sequences (empty until set_host_pool)
+        self.host_free: deque = deque()
+        self.host_ref: List[int] = []
+        self.swapped: Dict[int, list] = {}
 
     # ------------------------------------------------------------------ helpers
     def _no_blocks(self, needed: int) -> AllocError:
@@ -303,7 +322,14 @@ class BlockAllocatorModel:
 
     def free_seq(self, seq: int) -> None:
         """Release a finished sequence: walk its table from the last block to
-        the first; a block whose count reaches 0 goes to the free-list tail."""
+        the first; a block whose count reaches 0 goes to the free-list tail
+        (the host pool's, for a swapped-out sequence)."""
+        if seq in self.swapped:
+            for b in reversed(self.swapped.pop(seq)[0]):
+                self.host_ref[b] -= 1
+                if self.host_ref[b] == 0:
+                    self.host_free.append(b)
+            return
         if seq not in self.seqs:
             raise AllocError(E_INVAL, f"unknown sequence {seq}")
         table = self.seqs.pop(seq)[0]
@@ -311,6 +337,82 @@ class BlockAllocatorModel:
             self.ref[b] -= 1
             if self.ref[b] == 0:
                 self.free.append(b)
+
+    # ------------------------------------------------------------------ swap
+    def set_host_pool(self, num_blocks: int, free_order: Optional[Sequence[int]] = None) -> None:
+        if self.host_ref or num_blocks <= 0:
+            raise AllocError(E_INVAL, "the host pool is set once, with a positive size")
+        order = list(range(num_blocks)) if free_order is None else [int(b) for b in free_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise AllocError(E_INVAL, "host free_order must be a permutation")
+        self.host_free = deque(order)
+        self.host_ref = [0] * num_blocks
+
+    def _move(self, seqs, src_seqs, dst_seqs, src_ref, dst_ref, dst_take, src_release):
+        seqs = [int(x) for x in seqs]
+        if len(set(seqs)) != len(seqs) or any(x not in src_seqs for x in seqs):
+            raise AllocError(E_INVAL, "swap names an unknown, repeated or misplaced sequence")
+        order: List[int] = []
+        count: Dict[int, int] = {}
+        for x in seqs:
+            for b in src_seqs[x][0]:
+                if b not in count:
+                    count[b] = 0
+                    order.append(b)
+                count[b] += 1
+        for b in order:
+            if count[b] != src_ref[b]:
+                raise AllocError(E_INVAL, f"block {b} is shared with a sequence outside the group")
+        dst_free = self.free if dst_seqs is self.seqs else self.host_free
+        if len(order) > len(dst_free):
+            free = len(dst_free)
+            total = self.num_blocks if dst_seqs is self.seqs else len(self.host_ref)
+            raise AllocError(E_NOBLOCKS,
+                             f"failed to allocate {len(order)} blocks: {free} free of {total} total",
+                             len(order), free, total)
+        where: Dict[int, int] = {}
+        pairs: List[Tuple[int, int]] = []
+        for b in order:
+            d = dst_take()
+            dst_ref[d] = src_ref[b]
+            where[b] = d
+            pairs.append((b, d))
+        for b, _ in reversed(pairs):
+            src_ref[b] = 0
+            src_release(b)
+        for x in seqs:
+            entry = src_seqs.pop(x)
+            entry[0] = [where[b] for b in entry[0]]
+            dst_seqs[x] = entry
+        return pairs
+
+    def swap_out(self, seqs: Iterable[int]) -> List[Tuple[int, int]]:
+        """Move a group of sequences to the host pool; returns (device block,
+        host block) copy pairs.  The caller copies them before reusing the
+        released device blocks."""
+        if not self.host_ref:
+            raise AllocError(E_INVAL, "no host pool")
+
+        def take_host():
+            return self.host_free.popleft()
+
+        return self._move(seqs, self.seqs, self.swapped, self.ref, self.host_ref, take_host,
+                          self.free.append)
+
+    def swap_in(self, seqs: Iterable[int]) -> List[Tuple[int, int]]:
+        """Move a group of swapped-out sequences back; returns (host block,
+        device block) copy pairs, to be copied before the group is used."""
+        return self._move(seqs, self.swapped, self.seqs, self.host_ref, self.ref, self._take,
+                          self.host_free.append)
+
+    def host_free_list(self) -> List[int]:
+        return list(self.host_free)
+
+    def host_ref_counts(self) -> List[int]:
+        return list(self.host_ref)
+
+    def swapped_table(self, seq: int) -> List[int]:
+        return list(self.swapped[seq][0])
 
     # ------------------------------------------------------------------ views
     def table(self, seq: int) -> List[int]:
