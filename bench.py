@@ -23,6 +23,9 @@ Workloads (seeded synthetic inputs, see datagen):
   7  chunked prefill: 16 seqs = cached prefix U{0..2048} + a 512-token chunk;
      a step writes the chunk's K/V and runs the causal prefill attention;
      reported in attention TFLOP/s against the bf16 MFMA peak
+  8  swapping: 16 seqs x 2048 tokens swapped out to a pinned host pool and
+     back in; a step is one swap_blocks each way, reported in GB/s of blocks
+     moved against the host link (PCIe 5.0 x16, 64 GB/s each way)
 
 Prints one JSON line.  ``value`` = algorithmic KV bytes the decode reads per
 step / step time, in GB/s (1e9 B/s).  ``roofline`` reports the decode call
@@ -43,6 +46,7 @@ import numpy as np
 
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+HOST_LINK_PEAK_GBPS = 64.0   # PCIe 5.0 x16, each direction
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 WORKLOAD_NAMES = {
@@ -58,6 +62,8 @@ WORKLOAD_NAMES = {
        "question, 32 q / 8 kv heads, head_dim 128, bf16, block 16",
     7: "chunked prefill: 16 seqs = cached prefix U{0..2048} + 512 new tokens, 32 q / 8 kv heads, "
        "head_dim 128, bf16, block 16",
+    8: "swap out / in: 16 seqs x 2048 tokens, 8 kv heads, head_dim 128, bf16, block 16, "
+       "pinned host pool",
 }
 
 
@@ -66,7 +72,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6, 7])
+    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6, 7, 8])
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--partition-size", type=int, default=-1,
                     help="-1: balanced split (default); > 0: split-context partitions; 0: no split")
@@ -469,6 +475,60 @@ def cpu_baseline_prefill(w, tables, ctx, min_s: float = 10.0):
                       f"in {el:.1f} s, numpy/BLAS limited to 1 thread"}
 
 
+def run_swap(args, torch, pkv):
+    import datagen
+
+    S, n, Hkv, D, B = 16, 2048, 8, 128, args.block_size or 16
+    need = S * (-(-n // B))
+    nb = int(math.ceil(1.25 * need))
+    rng = np.random.default_rng(datagen.seed_for(8))
+    alloc = pkv.BlockAllocator(nb, B, rng.permutation(nb).astype(np.int32))
+    alloc.set_host_pool(need, rng.permutation(need).astype(np.int32))
+    for s_ in range(S):
+        alloc.add(s_, n)
+    group = list(range(S))
+    p_out = alloc.swap_out(group)
+    p_in = alloc.swap_in(group)
+    kc = to_dev(datagen.normal(rng, (nb, Hkv, B, D), "bf16"), torch)
+    vc = to_dev(datagen.normal(rng, (nb, Hkv, B, D), "bf16"), torch)
+    hk = torch.empty((need, Hkv, B, D), dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty((need, Hkv, B, D), dtype=torch.bfloat16, pin_memory=True)
+    d_out, d_in = to_dev(p_out, torch), to_dev(p_in, torch)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    out_ms = timed(lambda: pkv.swap_blocks(hk, hv, kc, vc, d_out, stream=stream))
+    in_ms = timed(lambda: pkv.swap_blocks(kc, vc, hk, hv, d_in, stream=stream))
+    moved = len(p_out) * 2 * Hkv * B * D * 2          # K and V bytes per direction
+    g_out, g_in = moved / (out_ms * 1e-3) / 1e9, moved / (in_ms * 1e-3) / 1e9
+    res = {
+        "metric": "swap GB/s (device to host, host to device)", "value": round(min(g_out, g_in), 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(out_ms + in_ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) K/V)",
+        "config": {"workload": WORKLOAD_NAMES[8], "blocks_per_direction": int(len(p_out)),
+                   "bytes_per_direction": int(moved)},
+        "swap_out_ms": round(out_ms, 4), "swap_in_ms": round(in_ms, 4),
+        "swap_out_gbps": round(g_out, 2), "swap_in_gbps": round(g_in, 2),
+        "roofline": {"bound": "host-link", "achieved": round(min(g_out, g_in), 2),
+                     "peak": HOST_LINK_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(min(g_out, g_in) / HOST_LINK_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "swap_blocks"},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -486,6 +546,9 @@ def main():
         return
     if args.workload == 7:
         run_prefill(args, torch, pkv)
+        return
+    if args.workload == 8:
+        run_swap(args, torch, pkv)
         return
     total = args.warmup + args.steps
     t_setup = time.perf_counter()

@@ -9,6 +9,7 @@
  *
  *   pkv_paged_kv_write          write new tokens' K/V into their slots
  *   pkv_copy_blocks             copy whole blocks (copy-on-write of shared blocks)
+ *   pkv_swap_blocks             copy whole blocks between HBM and host memory
  *   pkv_paged_attention_decode  one-query-per-sequence attention through the table
  *   pkv_paged_attention_prefill causal attention of several new tokens per sequence
  *   pkv_alloc_* / pkv_seq_*     free list, ref counts, lazy allocation, fork, CoW
@@ -391,6 +392,51 @@ int pkv_prefix_cache_lookup(const pkv_alloc* a, const int32_t* tokens, int32_t n
                             int32_t* blocks_out, int32_t* num_blocks_out);
 
 int pkv_prefix_cache_stats(const pkv_alloc* a, pkv_prefix_stats* out);
+
+/*
+ * Swapping (weishuz.com Month 2, section 02, row "swap to disk": blocks of a
+ * preempted request move to host memory and come back later).  The handle
+ * gets a second pool of host blocks; a group of sequences moves between the
+ * pools as a whole.  Every distinct block the group maps (first appearance
+ * in array order, then table order) gets a block from the target pool's
+ * free-list head and keeps its reference count; pairs_out receives the
+ * (source id, target id) pairs in that order, for pkv_swap_blocks; the
+ * source blocks are then released last pair first.  The pairs must be copied
+ * before the released blocks are reused (the next call that allocates).
+ * All-or-nothing.  Errors: PKV_EINVAL (no host pool, a sequence unknown,
+ * repeated or in the other pool, a block shared with a sequence outside the
+ * group, max_pairs below the group's table entries), PKV_ENOBLOCKS (target
+ * pool short; the message names the target pool's size).  A swapped-out
+ * sequence cannot append, fork or be tabled; pkv_seq_free releases its host
+ * blocks.
+ */
+int pkv_alloc_set_host_pool(pkv_alloc* a, int32_t num_host_blocks, const int32_t* free_order);
+int pkv_seq_swap_out(pkv_alloc* a, const int64_t* seqs, int32_t n, int32_t* pairs_out,
+                     int32_t max_pairs, int32_t* num_pairs_out);
+int pkv_seq_swap_in(pkv_alloc* a, const int64_t* seqs, int32_t n, int32_t* pairs_out,
+                    int32_t max_pairs, int32_t* num_pairs_out);
+int pkv_seq_swapped(const pkv_alloc* a, int64_t seq, int32_t* swapped_out);
+/* host pool's free list (head to tail) and reference counts, as pkv_alloc_export */
+int pkv_host_pool_export(const pkv_alloc* a, int32_t* free_fifo_out, int32_t* num_free_out,
+                         int32_t* ref_cnt_out);
+
+/*
+ * Copy whole blocks between two pools of the same block shape (c gives
+ * num_kv_heads, block_size, head_dim, dtype; c->num_blocks is ignored):
+ * for each i, K and V block pairs[i][1] of the destination pool take the
+ * contents of block pairs[i][0] of the source pool.  Either pool may be host
+ * memory the GPU can address (pinned, e.g. hipHostMalloc); this is how
+ * swapped blocks move between HBM and host memory, and the copy is then
+ * bound by the host link.
+ *   dst_k, dst_v     [dst_num_blocks, Hkv, B, D]
+ *   src_k, src_v     [src_num_blocks, Hkv, B, D]
+ *   pairs            device or pinned host, [num_pairs][2] int32 (src, dst)
+ * Ids outside their pool are skipped.  Destination blocks must be distinct
+ * and the pools must not overlap.  Errors: PKV_EINVAL, PKV_EHIP.
+ */
+int pkv_swap_blocks(void* dst_k, void* dst_v, int32_t dst_num_blocks, const void* src_k,
+                    const void* src_v, int32_t src_num_blocks, const pkv_cache_desc* c,
+                    const int32_t* pairs, int32_t num_pairs, void* stream);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* pkv_last_error(void);

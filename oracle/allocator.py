@@ -184,7 +184,7 @@ class BlockAllocatorModel:
         Takes ceil(n / B) blocks from the head of the free list and returns the
         slot of every prompt position (page 1, section 3(3), step 1)).
         """
-        if seq in self.seqs or num_tokens < 0:
+        if seq in self.seqs or seq in self.swapped or num_tokens < 0:
             raise AllocError(E_INVAL, f"bad add of sequence {seq}")
         B = self.block_size
         needed = -(-num_tokens // B)
@@ -205,7 +205,7 @@ class BlockAllocatorModel:
         free list (fresh ones, plus hits whose count was 0) are counted first.
         """
         tokens = [int(t) for t in tokens]
-        if seq in self.seqs:
+        if seq in self.seqs or seq in self.swapped:
             raise AllocError(E_INVAL, f"bad add of sequence {seq}")
         B = self.block_size
         n = len(tokens)
@@ -239,7 +239,7 @@ class BlockAllocatorModel:
     def fork(self, parent: int, child: int) -> None:
         """``child`` starts as a copy of ``parent``'s table; every block gains a
         reference (page 1, section 4, step (1))."""
-        if parent not in self.seqs or child in self.seqs:
+        if parent not in self.seqs or child in self.seqs or child in self.swapped:
             raise AllocError(E_INVAL, f"bad fork {parent} -> {child}")
         table, length, toks = self.seqs[parent]
         for b in table:

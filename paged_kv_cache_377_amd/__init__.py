@@ -28,6 +28,7 @@ from ._lib import (  # noqa: F401
     paged_attention_decode,
     paged_attention_prefill,
     paged_kv_write,
+    swap_blocks,
     validate_copy,
     validate_decode,
     validate_prefill,

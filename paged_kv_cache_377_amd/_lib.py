@@ -85,6 +85,12 @@ _SIGS = {
     "pkv_step_append_tokens": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "pkv_prefix_cache_lookup": (_i32, [_vp, _vp, _i32, _vp, _vp]),
     "pkv_prefix_cache_stats": (_i32, [_vp, _P(PrefixStats)]),
+    "pkv_alloc_set_host_pool": (_i32, [_vp, _i32, _vp]),
+    "pkv_seq_swap_out": (_i32, [_vp, _vp, _i32, _vp, _i32, _vp]),
+    "pkv_seq_swap_in": (_i32, [_vp, _vp, _i32, _vp, _i32, _vp]),
+    "pkv_seq_swapped": (_i32, [_vp, _i64, _vp]),
+    "pkv_host_pool_export": (_i32, [_vp, _vp, _vp, _vp]),
+    "pkv_swap_blocks": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _P(CacheDesc), _vp, _i32, _vp]),
     "pkv_last_error": (ctypes.c_char_p, []),
 }
 
@@ -249,6 +255,21 @@ def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens
         int(max_new_tokens), int(max_context_len), float(scale), _stream(stream)))
 
 
+def swap_blocks(dst_k, dst_v, src_k, src_v, pairs, stream=None) -> None:
+    """Copy blocks pairs[i][0] of (src_k, src_v) into blocks pairs[i][1] of
+    (dst_k, dst_v); pools [NB, Hkv, B, D] of one block shape, either one may
+    be pinned host memory.  ``pairs``: [n, 2] int32, device or pinned host."""
+    torch = _torch()
+    if pairs.dtype != torch.int32 or (pairs.numel() and (pairs.dim() != 2 or pairs.shape[1] != 2)):
+        raise PagedKVError(PKV_EINVAL, "pairs must be [n, 2] int32")
+    if dst_k.shape[1:] != src_k.shape[1:] or dst_k.dtype != src_k.dtype:
+        raise PagedKVError(PKV_EINVAL, "pools differ in block shape or dtype")
+    desc = cache_desc(dst_k)
+    _check(lib().pkv_swap_blocks(_ptr(dst_k), _ptr(dst_v), dst_k.shape[0], _ptr(src_k), _ptr(src_v),
+                                 src_k.shape[0], ctypes.byref(desc), _ptr(pairs),
+                                 pairs.shape[0] if pairs.numel() else 0, _stream(stream)))
+
+
 # --------------------------------------------------------- host checks
 
 def _np(a, dtype):
@@ -381,6 +402,44 @@ class BlockAllocator:
 
     def free(self, seq: int) -> None:
         _check(self._l.pkv_seq_free(self._h, seq))
+
+    def set_host_pool(self, num_blocks: int, free_order=None) -> None:
+        order = None if free_order is None else _np(free_order, np.int32)
+        if order is not None and order.size != num_blocks:
+            raise PagedKVError(PKV_EINVAL, "host free_order must have num_blocks entries")
+        _check(self._l.pkv_alloc_set_host_pool(self._h, num_blocks,
+                                               None if order is None else order.ctypes.data))
+        self.num_host_blocks = num_blocks
+
+    def _swap(self, fn, seqs) -> np.ndarray:
+        s = _np(seqs, np.int64)
+        cap = sum(self.info(int(x))[1] for x in s) if s.size else 0
+        pairs = np.empty((max(cap, 1), 2), dtype=np.int32)
+        n = ctypes.c_int32()
+        _check(fn(self._h, s.ctypes.data, s.size, pairs.ctypes.data, cap, ctypes.byref(n)))
+        return pairs[: n.value].copy()
+
+    def swap_out(self, seqs) -> np.ndarray:
+        """Move a group to the host pool: (device id, host id) pairs [k, 2]."""
+        return self._swap(self._l.pkv_seq_swap_out, seqs)
+
+    def swap_in(self, seqs) -> np.ndarray:
+        """Move a swapped-out group back: (host id, device id) pairs [k, 2]."""
+        return self._swap(self._l.pkv_seq_swap_in, seqs)
+
+    def swapped(self, seq: int) -> bool:
+        v = ctypes.c_int32()
+        _check(self._l.pkv_seq_swapped(self._h, seq, ctypes.byref(v)))
+        return bool(v.value)
+
+    def host_export(self) -> Tuple[List[int], List[int]]:
+        n = getattr(self, "num_host_blocks", 0)
+        fifo = np.empty(max(n, 1), dtype=np.int32)
+        ref = np.empty(max(n, 1), dtype=np.int32)
+        nfree = ctypes.c_int32()
+        _check(self._l.pkv_host_pool_export(self._h, fifo.ctypes.data, ctypes.byref(nfree),
+                                            ref.ctypes.data))
+        return fifo[: nfree.value].tolist(), ref[:n].tolist()
 
     def info(self, seq: int) -> Tuple[int, int]:
         n, b = ctypes.c_int32(), ctypes.c_int32()

@@ -83,6 +83,7 @@ typedef struct {
   uint32_t stamp;    /* last batch step that named this sequence           */
   uint8_t state;     /* 0 empty, 1 live, 2 deleted                         */
   uint8_t tracked;   /* token ids known for every position (prefix cache)  */
+  uint8_t swapped;   /* table holds host-pool block ids                     */
   uint64_t chain;    /* chain hash through the last full block             */
   int32_t* toks;     /* ids of the partial last block's tokens, [B]        */
 } seq_entry;
@@ -115,6 +116,14 @@ struct pkv_alloc {
   int64_t hits;
   int64_t queries;
   int64_t evictions;
+  /* host pool for swapped-out sequences (0 blocks until set) */
+  int32_t hnum;
+  int32_t* hfifo;    /* ring buffer of free host ids                        */
+  int32_t hhead;
+  int32_t hnfree;
+  int32_t* href;
+  int32_t* dmark;    /* per-block scratch of a swap, all zero between calls */
+  int32_t* hmark;
 };
 
 static uint64_t mix64(uint64_t x) {
@@ -367,6 +376,10 @@ void pkv_alloc_destroy(pkv_alloc* a) {
   free(a->btok);
   free(a->bcached);
   free(a->map);
+  free(a->hfifo);
+  free(a->href);
+  free(a->dmark);
+  free(a->hmark);
   free(a);
 }
 
@@ -537,6 +550,7 @@ int pkv_seq_fork(pkv_alloc* a, int64_t parent, int64_t child) {
   if (!a) return pkv__fail(PKV_EINVAL, "allocator handle is NULL");
   seq_entry* p = find(a, parent);
   if (!p) return pkv__fail(PKV_EINVAL, "unknown parent sequence %lld", (long long)parent);
+  if (p->swapped) return pkv__fail(PKV_EINVAL, "sequence %lld is swapped out", (long long)parent);
   if (find(a, child)) return pkv__fail(PKV_EINVAL, "sequence %lld already exists", (long long)child);
   /* insert may move the table: remember the parent's contents by id */
   seq_entry* c = insert(a, child);
@@ -614,6 +628,7 @@ static int seq_append(pkv_alloc* a, int64_t seq, int64_t* slot_out, int32_t cow_
   if (!slot_out) return pkv__fail(PKV_EINVAL, "slot_out is NULL");
   seq_entry* e = find(a, seq);
   if (!e) return pkv__fail(PKV_EINVAL, "unknown sequence %lld", (long long)seq);
+  if (e->swapped) return pkv__fail(PKV_EINVAL, "sequence %lld is swapped out", (long long)seq);
   if (e->len == INT32_MAX) return pkv__fail(PKV_EINVAL, "sequence %lld is full", (long long)seq);
   if (append_needs(a, e) > a->nfree) return no_blocks(a, 1);
   if (e->len % a->block_size == 0 && reserve_blocks(e, e->nblk + 1) != PKV_OK) return PKV_EINVAL;
@@ -650,8 +665,9 @@ static int step_append(pkv_alloc* a, const int64_t* seqs, const int32_t* tokens,
   /* pass 1: ids known and distinct; room in every table */
   for (int32_t i = 0; i < n; ++i) {
     seq_entry* e = find(a, seqs[i]);
-    if (!e || e->stamp == stamp)
-      return pkv__fail(PKV_EINVAL, "step names an unknown or repeated sequence (%lld at %d)",
+    if (!e || e->stamp == stamp || e->swapped)
+      return pkv__fail(PKV_EINVAL,
+                       "step names an unknown, repeated or swapped-out sequence (%lld at %d)",
                        (long long)seqs[i], i);
     e->stamp = stamp;
     if (e->len == INT32_MAX) return pkv__fail(PKV_EINVAL, "sequence %lld is full", (long long)seqs[i]);
@@ -707,6 +723,180 @@ int pkv_step_append_tokens(pkv_alloc* a, const int64_t* seqs, const int32_t* tok
   return step_append(a, seqs, tokens, n, slots_out, cow_pairs_out, num_cow_out);
 }
 
+/* ------------------------------------------------------------- swapping */
+
+static int32_t host_take(pkv_alloc* a) {
+  int32_t h = a->hfifo[a->hhead];
+  a->hhead = (a->hhead + 1 == a->hnum) ? 0 : a->hhead + 1;
+  a->hnfree--;
+  return h;
+}
+
+static void host_return(pkv_alloc* a, int32_t h) {
+  int64_t tail = (int64_t)a->hhead + a->hnfree;
+  if (tail >= a->hnum) tail -= a->hnum;
+  a->hfifo[tail] = h;
+  a->hnfree++;
+}
+
+int pkv_alloc_set_host_pool(pkv_alloc* a, int32_t num_host_blocks, const int32_t* free_order) {
+  pkv__clear_error();
+  if (!a) return pkv__fail(PKV_EINVAL, "allocator handle is NULL");
+  if (a->hnum) return pkv__fail(PKV_EINVAL, "the host pool is already set");
+  if (num_host_blocks <= 0) return pkv__fail(PKV_EINVAL, "num_host_blocks %d <= 0", num_host_blocks);
+  const size_t n = (size_t)num_host_blocks;
+  int32_t* fifo = (int32_t*)malloc(n * sizeof(int32_t));
+  int32_t* ref = (int32_t*)calloc(n, sizeof(int32_t));
+  int32_t* hmark = (int32_t*)calloc(n, sizeof(int32_t));
+  int32_t* dmark = (int32_t*)calloc((size_t)a->num_blocks, sizeof(int32_t));
+  if (!fifo || !ref || !hmark || !dmark) {
+    free(fifo); free(ref); free(hmark); free(dmark);
+    return pkv__fail(PKV_EINVAL, "out of host memory");
+  }
+  for (int32_t i = 0; i < num_host_blocks; ++i) {
+    int32_t h = free_order ? free_order[i] : i;
+    if (h < 0 || h >= num_host_blocks || hmark[h]) {
+      free(fifo); free(ref); free(hmark); free(dmark);
+      return pkv__fail(PKV_EINVAL, "host free_order is not a permutation of 0..%d (entry %d = %d)",
+                       num_host_blocks - 1, i, h);
+    }
+    hmark[h] = 1;
+    fifo[i] = h;
+  }
+  memset(hmark, 0, n * sizeof(int32_t));
+  a->hnum = num_host_blocks;
+  a->hfifo = fifo;
+  a->href = ref;
+  a->hmark = hmark;
+  a->dmark = dmark;
+  a->hhead = 0;
+  a->hnfree = num_host_blocks;
+  return PKV_OK;
+}
+
+/* Move a group of sequences between the pools (out: device -> host).  Each
+ * distinct block of the group (first appearance in array, then table order)
+ * goes to a block taken from the target pool; pairs_out receives (source,
+ * target) ids in that order; the source blocks are released last pair first. */
+static int swap_group(pkv_alloc* a, const int64_t* seqs, int32_t n, int32_t* pairs_out,
+                      int32_t max_pairs, int32_t* num_pairs_out, int out) {
+  pkv__clear_error();
+  if (!a) return pkv__fail(PKV_EINVAL, "allocator handle is NULL");
+  if (!a->hnum) return pkv__fail(PKV_EINVAL, "no host pool: call pkv_alloc_set_host_pool first");
+  if (n < 0 || (n > 0 && (!seqs || !pairs_out)) || !num_pairs_out)
+    return pkv__fail(PKV_EINVAL, "bad swap arguments");
+  uint32_t stamp = ++a->step_no;
+  if (stamp == 0) {
+    for (size_t i = 0; i < a->tcap; ++i) a->tab[i].stamp = 0;
+    stamp = a->step_no = 1;
+  }
+  int64_t total = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    seq_entry* e = find(a, seqs[i]);
+    if (!e || e->stamp == stamp || e->swapped != (out ? 0 : 1))
+      return pkv__fail(PKV_EINVAL, "swap names an unknown, repeated or misplaced sequence (%lld at %d)",
+                       (long long)seqs[i], i);
+    e->stamp = stamp;
+    total += e->nblk;
+  }
+  if (total > max_pairs)
+    return pkv__fail(PKV_EINVAL, "pairs_out holds %d pairs, the group maps %lld blocks", max_pairs,
+                     (long long)total);
+  int32_t* src_ref = out ? a->ref : a->href;
+  int32_t* cnt = out ? a->dmark : a->hmark;
+  int32_t* order = (int32_t*)malloc((size_t)(total > 0 ? total : 1) * sizeof(int32_t));
+  if (!order) return pkv__fail(PKV_EINVAL, "out of host memory");
+  int32_t nd = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const seq_entry* e = find(a, seqs[i]);
+    for (int32_t j = 0; j < e->nblk; ++j) {
+      int32_t b = e->blocks[j];
+      if (cnt[b]++ == 0) order[nd++] = b;
+    }
+  }
+  int rc = PKV_OK;
+  for (int32_t k = 0; k < nd && rc == PKV_OK; ++k)
+    if (cnt[order[k]] != src_ref[order[k]])
+      rc = pkv__fail(PKV_EINVAL, "block %d is shared with a sequence outside the group", order[k]);
+  const int32_t dst_free = out ? a->hnfree : a->nfree;
+  if (rc == PKV_OK && nd > dst_free)
+    rc = pkv__fail(PKV_ENOBLOCKS, "failed to allocate %d blocks: %d free of %d total", nd, dst_free,
+                   out ? a->hnum : a->num_blocks);
+  if (rc != PKV_OK) {
+    for (int32_t k = 0; k < nd; ++k) cnt[order[k]] = 0;
+    free(order);
+    return rc;
+  }
+  /* apply: from here on nothing fails */
+  for (int32_t k = 0; k < nd; ++k) {
+    const int32_t b = order[k];
+    int32_t d;
+    if (out) {
+      d = host_take(a);
+      a->href[d] = a->ref[b];
+    } else {
+      d = take_block(a);
+      a->ref[d] = a->href[b];
+    }
+    pairs_out[2 * k] = b;
+    pairs_out[2 * k + 1] = d;
+    cnt[b] = d + 1; /* from now on: where b went */
+  }
+  for (int32_t k = nd - 1; k >= 0; --k) {
+    const int32_t b = order[k];
+    if (out) {
+      a->ref[b] = 0;
+      return_block(a, b);
+    } else {
+      a->href[b] = 0;
+      host_return(a, b);
+    }
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    seq_entry* e = find(a, seqs[i]);
+    for (int32_t j = 0; j < e->nblk; ++j) e->blocks[j] = cnt[e->blocks[j]] - 1;
+    e->swapped = out ? 1 : 0;
+  }
+  for (int32_t k = 0; k < nd; ++k) cnt[order[k]] = 0;
+  free(order);
+  *num_pairs_out = nd;
+  return PKV_OK;
+}
+
+int pkv_seq_swap_out(pkv_alloc* a, const int64_t* seqs, int32_t n, int32_t* pairs_out,
+                     int32_t max_pairs, int32_t* num_pairs_out) {
+  return swap_group(a, seqs, n, pairs_out, max_pairs, num_pairs_out, 1);
+}
+
+int pkv_seq_swap_in(pkv_alloc* a, const int64_t* seqs, int32_t n, int32_t* pairs_out,
+                    int32_t max_pairs, int32_t* num_pairs_out) {
+  return swap_group(a, seqs, n, pairs_out, max_pairs, num_pairs_out, 0);
+}
+
+int pkv_seq_swapped(const pkv_alloc* a, int64_t seq, int32_t* swapped_out) {
+  pkv__clear_error();
+  if (!a || !swapped_out) return pkv__fail(PKV_EINVAL, "NULL argument");
+  const seq_entry* e = find(a, seq);
+  if (!e) return pkv__fail(PKV_EINVAL, "unknown sequence %lld", (long long)seq);
+  *swapped_out = e->swapped;
+  return PKV_OK;
+}
+
+int pkv_host_pool_export(const pkv_alloc* a, int32_t* free_fifo_out, int32_t* num_free_out,
+                         int32_t* ref_cnt_out) {
+  pkv__clear_error();
+  if (!a) return pkv__fail(PKV_EINVAL, "allocator handle is NULL");
+  if (free_fifo_out)
+    for (int32_t i = 0; i < a->hnfree; ++i) {
+      int64_t j = (int64_t)a->hhead + i;
+      if (j >= a->hnum) j -= a->hnum;
+      free_fifo_out[i] = a->hfifo[j];
+    }
+  if (num_free_out) *num_free_out = a->hnfree;
+  if (ref_cnt_out && a->hnum) memcpy(ref_cnt_out, a->href, (size_t)a->hnum * sizeof(int32_t));
+  return PKV_OK;
+}
+
 int pkv_seq_free(pkv_alloc* a, int64_t seq) {
   pkv__clear_error();
   if (!a) return pkv__fail(PKV_EINVAL, "allocator handle is NULL");
@@ -714,7 +904,11 @@ int pkv_seq_free(pkv_alloc* a, int64_t seq) {
   if (!e) return pkv__fail(PKV_EINVAL, "unknown sequence %lld", (long long)seq);
   for (int32_t i = e->nblk - 1; i >= 0; --i) {
     int32_t b = e->blocks[i];
-    if (--a->ref[b] == 0) return_block(a, b);
+    if (e->swapped) {
+      if (--a->href[b] == 0) host_return(a, b);
+    } else if (--a->ref[b] == 0) {
+      return_block(a, b);
+    }
   }
   erase(a, e);
   return PKV_OK;
@@ -740,6 +934,8 @@ int pkv_build_tables(const pkv_alloc* a, const int64_t* seqs, int32_t n, int32_t
   for (int32_t i = 0; i < n; ++i) {
     const seq_entry* e = find(a, seqs[i]);
     if (!e) return pkv__fail(PKV_EINVAL, "unknown sequence %lld", (long long)seqs[i]);
+    if (e->swapped)
+      return pkv__fail(PKV_EINVAL, "sequence %lld is swapped out", (long long)seqs[i]);
     if (e->nblk > width)
       return pkv__fail(PKV_EINVAL, "sequence %lld holds %d blocks, more than width %d",
                        (long long)seqs[i], e->nblk, width);
@@ -763,7 +959,7 @@ int pkv_alloc_stats(const pkv_alloc* a, pkv_stats* out) {
   int64_t logical = 0;
   for (size_t i = 0; i < a->tcap; ++i) {
     const seq_entry* e = &a->tab[i];
-    if (e->state != 1) continue;
+    if (e->state != 1 || e->swapped) continue;
     logical += e->len;
     for (int32_t j = 0; j < e->nblk; ++j) {
       int32_t f = e->len - j * B;

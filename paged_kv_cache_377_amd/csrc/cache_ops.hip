@@ -73,6 +73,26 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
   v_cache[(int64_t)dst * block_chunks + c] = vr;
 }
 
+// Swap copy: like copy_blocks, but source and destination are two pools
+// (either may be pinned host memory); one 16-byte piece of K and of V per
+// thread.
+__global__ __launch_bounds__(kThreads) void swap_blocks_kernel(
+    uint4* __restrict__ dst_k, uint4* __restrict__ dst_v, int32_t dst_num_blocks,
+    const uint4* __restrict__ src_k, const uint4* __restrict__ src_v, int32_t src_num_blocks,
+    const int32_t* __restrict__ pairs, int32_t block_chunks, int32_t groups_per_block) {
+  const int32_t pair = blockIdx.x / groups_per_block;
+  const int32_t grp = blockIdx.x - pair * groups_per_block;
+  const int32_t c = grp * kThreads + threadIdx.x;
+  const int32_t src = pairs[2 * pair];
+  const int32_t dst = pairs[2 * pair + 1];
+  if (c >= block_chunks || src < 0 || src >= src_num_blocks || dst < 0 || dst >= dst_num_blocks)
+    return;
+  const uint4 kr = src_k[(int64_t)src * block_chunks + c];
+  const uint4 vr = src_v[(int64_t)src * block_chunks + c];
+  dst_k[(int64_t)dst * block_chunks + c] = kr;
+  dst_v[(int64_t)dst * block_chunks + c] = vr;
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int elem_bytes(int32_t dtype) { return dtype == PKV_BF16 ? 2 : 4; }
@@ -136,5 +156,40 @@ extern "C" int pkv_copy_blocks(void* k_cache, void* v_cache, const pkv_cache_des
                      block_chunks, groups, c->num_blocks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return pkv__fail(PKV_EHIP, "copy_blocks launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+extern "C" int pkv_swap_blocks(void* dst_k, void* dst_v, int32_t dst_num_blocks, const void* src_k,
+                               const void* src_v, int32_t src_num_blocks, const pkv_cache_desc* c,
+                               const int32_t* pairs, int32_t num_pairs, void* stream) {
+  pkv__clear_error();
+  if (!c) return pkv__fail(PKV_EINVAL, "cache descriptor is NULL");
+  if (c->num_kv_heads <= 0 || c->block_size <= 0 || c->head_dim <= 0 ||
+      (c->dtype != PKV_F32 && c->dtype != PKV_BF16))
+    return pkv__fail(PKV_EINVAL, "bad block shape in the cache descriptor");
+  if (dst_num_blocks <= 0 || src_num_blocks <= 0)
+    return pkv__fail(PKV_EINVAL, "pool sizes must be positive (dst %d, src %d)", dst_num_blocks,
+                     src_num_blocks);
+  if (num_pairs < 0) return pkv__fail(PKV_EINVAL, "num_pairs %d < 0", num_pairs);
+  if (num_pairs == 0) return PKV_OK;
+  if (!dst_k || !dst_v || !src_k || !src_v || !pairs) return pkv__fail(PKV_EINVAL, "NULL pointer");
+  if (!aligned16(dst_k) || !aligned16(dst_v) || !aligned16(src_k) || !aligned16(src_v) ||
+      ((uintptr_t)pairs & 7u))
+    return pkv__fail(PKV_EINVAL, "pools must be 16-byte aligned, pairs 8-byte aligned");
+  const int64_t block_bytes =
+      (int64_t)c->num_kv_heads * c->block_size * c->head_dim * elem_bytes(c->dtype);
+  if (block_bytes % 16 != 0 || block_bytes / 16 > INT32_MAX)
+    return pkv__fail(PKV_EUNSUPPORTED, "block of %lld bytes is not a multiple of 16",
+                     (long long)block_bytes);
+  const int32_t block_chunks = (int32_t)(block_bytes / 16);
+  const int32_t groups = (block_chunks + kThreads - 1) / kThreads;
+  const int64_t grid = (int64_t)num_pairs * groups;
+  if (grid > INT32_MAX) return pkv__fail(PKV_EINVAL, "swap too large");
+  hipLaunchKernelGGL(swap_blocks_kernel, dim3((uint32_t)grid), dim3(kThreads), 0,
+                     (hipStream_t)stream, (uint4*)dst_k, (uint4*)dst_v, dst_num_blocks,
+                     (const uint4*)src_k, (const uint4*)src_v, src_num_blocks, pairs, block_chunks,
+                     groups);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return pkv__fail(PKV_EHIP, "swap_blocks launch: %s", hipGetErrorString(e));
   return PKV_OK;
 }

@@ -3,7 +3,7 @@
  * Input lines:  N B perm...  then  add s n | fork p c | append s |
  *               step k s1..sk | free s | table s | prefix |
  *               addt s k t1..tk | appt s t | stept k s1..sk t1..tk |
- *               look k t1..tk
+ *               look k t1..tk | hpool n | sout k s1..sk | sin k s1..sk
  * Output: one line per op with the return code and results. */
 #include <stdio.h>
 #include <stdlib.h>
@@ -22,7 +22,26 @@ int main(void) {
   if (!a) return 3;
   char op[16];
   while (scanf("%15s", op) == 1) {
-    if (strcmp(op, "prefix") == 0) {
+    if (strcmp(op, "hpool") == 0) {
+      int hn;
+      if (scanf("%d", &hn) != 1) return 2;
+      printf("hpool %d\n", pkv_alloc_set_host_pool(a, hn, NULL));
+    } else if (strcmp(op, "sout") == 0 || strcmp(op, "sin") == 0) {
+      int k;
+      if (scanf("%d", &k) != 1 || k < 0) return 2;
+      int64_t* ids = malloc(sizeof(int64_t) * (k > 0 ? k : 1));
+      for (int i = 0; i < k; ++i) { long long x; if (scanf("%lld", &x) != 1) return 2; ids[i] = x; }
+      int cap = 0;
+      for (int i = 0; i < k; ++i) { int32_t len, nb; if (pkv_seq_info(a, ids[i], &len, &nb) == 0) cap += nb; }
+      int32_t* pairs = malloc(sizeof(int32_t) * 2 * (cap > 0 ? cap : 1));
+      int32_t np = 0;
+      int rc = op[1] == 'o' ? pkv_seq_swap_out(a, ids, k, pairs, cap, &np)
+                            : pkv_seq_swap_in(a, ids, k, pairs, cap, &np);
+      printf("%s %d", op, rc);
+      if (rc == 0) for (int i = 0; i < np; ++i) printf(" %d %d", pairs[2 * i], pairs[2 * i + 1]);
+      printf("\n");
+      free(ids); free(pairs);
+    } else if (strcmp(op, "prefix") == 0) {
       printf("prefix %d\n", pkv_prefix_cache_enable(a));
     } else if (strcmp(op, "addt") == 0) {
       long long s; int k;
@@ -120,8 +139,12 @@ int main(void) {
       long long s; int32_t len, nb;
       if (scanf("%lld", &s) != 1) return 2;
       int rc = pkv_seq_info(a, s, &len, &nb);
+      int32_t sw = 0;
+      if (rc == 0) pkv_seq_swapped(a, s, &sw);
       printf("table %d", rc);
-      if (rc == 0) {
+      if (rc == 0 && sw) {
+        printf(" %d : swapped", len);
+      } else if (rc == 0) {
         int32_t* row = malloc(sizeof(int32_t) * (nb > 0 ? nb : 1));
         int64_t id = s; int32_t l2;
         pkv_build_tables(a, &id, 1, row, nb, &l2);
@@ -145,6 +168,15 @@ int main(void) {
   printf("\n");
   pkv_stats st;
   pkv_alloc_stats(a, &st);
+  int32_t* hf = malloc(sizeof(int32_t) * 4096);
+  int32_t* hr = malloc(sizeof(int32_t) * 4096);
+  int32_t hnf = 0;
+  if (pkv_host_pool_export(a, hf, &hnf, NULL) == 0 && hnf > 0) {
+    printf("host free");
+    for (int i = 0; i < hnf; ++i) printf(" %d", hf[i]);
+    printf("\n");
+  }
+  free(hf); free(hr);
   pkv_prefix_stats ps;
   pkv_prefix_cache_stats(a, &ps);
   if (ps.enabled)

@@ -319,6 +319,71 @@ def test_sanitizer_replay_prefix_cache_matches_oracle(replay_bin, seed):
     assert r.stdout.strip().splitlines() == _oracle_prefix_replay(lines, B, N, order)
 
 
+def _swap_replay_lines(seed):
+    rnd = random.Random(900 + seed)
+    B = rnd.choice([1, 2, 4])
+    N, H = rnd.randrange(3, 24), rnd.randrange(2, 24)
+    order = rnd.sample(range(N), N)
+    ids = list(range(10))
+    lines = [f"{N} {B} " + " ".join(map(str, order)), f"hpool {H}"]
+    for _ in range(400):
+        r = rnd.random()
+        s = rnd.choice(ids)
+        if r < 0.2:
+            lines.append(f"add {s} {rnd.randint(0, 3 * B)}")
+        elif r < 0.3:
+            lines.append(f"fork {s} {rnd.choice(ids)}")
+        elif r < 0.5:
+            k = rnd.randint(0, 4)
+            lines.append(f"step {k} " + " ".join(str(rnd.choice(ids)) for _ in range(k)))
+        elif r < 0.65:
+            k = rnd.randint(0, 3)
+            lines.append(f"sout {k} " + " ".join(str(rnd.choice(ids)) for _ in range(k)))
+        elif r < 0.8:
+            k = rnd.randint(0, 3)
+            lines.append(f"sin {k} " + " ".join(str(rnd.choice(ids)) for _ in range(k)))
+        elif r < 0.9:
+            lines.append(f"free {s}")
+        else:
+            lines.append(f"table {s}")
+    return lines, B, N, order, H
+
+
+def _oracle_swap_replay(lines, B, N, order, H):
+    o = BlockAllocatorModel(N, B, order)
+    o.set_host_pool(H)
+    out = ["hpool 0"]
+    for ln in lines[2:]:
+        f = ln.split()
+        if f[0] in ("sout", "sin"):
+            k = int(f[1])
+            seqs = [int(x) for x in f[2:2 + k]]
+            try:
+                pairs = o.swap_out(seqs) if f[0] == "sout" else o.swap_in(seqs)
+                out.append(f"{f[0]} 0" + "".join(f" {a} {b}" for a, b in pairs))
+            except AllocError as e:
+                out.append(f"{f[0]} {e.code}")
+        elif f[0] == "table" and int(f[1]) in o.swapped:
+            out.append(f"table 0 {o.swapped[int(f[1])][1]} : swapped")
+        else:
+            out.extend(_oracle_replay([lines[0], ln], B, N, order, model=o)[:-1])
+    out.append("final free" + "".join(f" {b}" for b in o.free_list()) + " | ref" +
+               "".join(f" {r}" for r in o.ref_counts()))
+    if o.host_free_list():
+        out.append("host free" + "".join(f" {b}" for b in o.host_free_list()))
+    return out
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_sanitizer_replay_swap_matches_oracle(replay_bin, seed):
+    lines, B, N, order, H = _swap_replay_lines(seed)
+    r = subprocess.run([replay_bin], input="\n".join(lines) + "\n", capture_output=True,
+                       text=True, timeout=60)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "ERROR: AddressSanitizer" not in r.stderr and "runtime error" not in r.stderr
+    assert r.stdout.strip().splitlines() == _oracle_swap_replay(lines, B, N, order, H)
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_sanitizer_replay_matches_oracle(replay_bin, seed):
     lines, B, N, order = _replay_lines(seed)

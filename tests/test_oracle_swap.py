@@ -140,3 +140,17 @@ def test_random_streams_every_sequence_reads_its_history(seed):
         except AllocError as e:
             assert e.code in (E_INVAL, E_NOBLOCKS)
         _check(m, w)
+
+
+def test_swapped_ids_stay_taken():
+    m = BlockAllocatorModel(8, 2)
+    m.set_host_pool(4)
+    m.add(1, 3)
+    m.swap_out([1])
+    for call in (lambda: m.add(1, 1), lambda: m.add_tokens(1, [5]), lambda: m.fork(1, 2)):
+        with pytest.raises(AllocError) as ei:
+            call()
+        assert ei.value.code == E_INVAL
+    m.add(2, 1)
+    with pytest.raises(AllocError):
+        m.fork(2, 1)
