@@ -42,6 +42,8 @@
 
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "pkv_internal.h"
 
 namespace {
@@ -196,7 +198,7 @@ __device__ inline void stage_store(const Stage<D>& st, uint16_t* lk, uint16_t* l
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(
+__global__ __launch_bounds__(kThreads, 3) void prefill_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, int32_t max_blocks_per_seq,
@@ -277,7 +279,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   }
   __syncthreads();
 
-  for (int kt = 0; kt < ntiles; ++kt) {
+  // One key tile; MASKED tiles reach past the workgroup's first position and
+  // apply the causal mask, the others (all but the last one or two) skip it.
+  auto tile = [&](const int kt, auto masked_tag) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
     const int buf = kt & 1;
     stage_load<D>(st, k_cache, v_cache, (kt + 1) * kKeys, n, log2b, g, num_kv_heads, num_blocks);
     stage_entries<D>(st, table, (kt + 2) * kKeys, n, log2b);
@@ -300,11 +305,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     }
 
     // Online softmax of each row; P^T operands (hi and lo parts) in the S^T
-    // key order.  Only tiles that reach past the workgroup's first position
-    // need the causal mask (wave-uniform test).
+    // key order.
     uint4 pb[2], pl[2];
     const int tbase = kt * kKeys + 4 * grp;
-    const bool masked = (kt + 1) * kKeys - 1 > first + j0;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       // raw logits; qscale > 0, so the scaled maximum is qscale * max
@@ -316,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
         for (int r = 0; r < 4; ++r) {
           const int t = tbase + 16 * h + r;
           x[h][r] = sc[c][h][r];
-          if (masked) x[h][r] = t <= pos[c] ? x[h][r] : -INFINITY;
+          if constexpr (kMasked) x[h][r] = t <= pos[c] ? x[h][r] : -INFINITY;
           mx = fmaxf(mx, x[h][r]);
         }
       mx = rows_max(mx) * qscale;
@@ -368,7 +371,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 
     stage_store<D>(st, lds[buf ^ 1][0], lds[buf ^ 1][1]);
     __syncthreads();
-  }
+  };
+  // tiles whose last key is <= the workgroup's first position need no mask
+  const int kt_plain = min(ntiles, max(0, (first + j0 + 1) / kKeys));
+  int kt = 0;
+  for (; kt < kt_plain; ++kt) tile(kt, std::false_type{});
+  for (; kt < ntiles; ++kt) tile(kt, std::true_type{});
 
   // Normalise and store: lane holds dims 16 t + 4 grp + r of its rows.
 #pragma unroll
