@@ -4,8 +4,9 @@
 
 One step is one pass of the whole hot path over one batch: the host allocator
 appends one token to every sequence (lazy allocation, copy-on-write pairs),
-then on the GPU copy_blocks (when the step produced pairs), paged_kv_write of
-the new tokens, and paged_attention_decode (partition + reduce).  The
+then on the GPU copy_blocks (when the step produced pairs) and the decode with
+the new tokens' K/V written by the same launch (pkv_paged_attention_decode_
+append; --unfused: paged_kv_write, then paged_attention_decode).  The
 allocator's output for every step is computed before the timed region and
 uploaded, so the timed region starts with every input resident in HBM.
 
@@ -79,6 +80,9 @@ def parse():
     ap.add_argument("--replicas", type=int, default=1,
                     help="rotate over R copies of the KV pool (step i uses copy i %% R)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="run paged_kv_write and the decode as two launches instead of the fused "
+                         "append + decode")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the benchmark, time a plain device copy of this many MiB "
                          "(the reference kernel for HBM counter calibration and the copy ceiling)")
@@ -577,11 +581,18 @@ def main():
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
+    fused = not args.unfused and sh.dtype == "bf16" and args.partition_size == -1
+
     def step(i):
         d = dsteps[i]
         kc, vc = kcs[i % R], vcs[i % R]
         if d["pairs"] is not None:
             pkv.copy_blocks(kc, vc, d["pairs"], stream=stream)
+        if fused:   # the new token's K/V written by the decode launch itself
+            pkv.paged_attention_decode_append(out, d["q"], d["k"], d["v"], kc, vc, d["tables"],
+                                              d["ctx"], sh.scale, d["max_ctx"],
+                                              workspace=workspace, stream=stream)
+            return
         pkv.paged_kv_write(d["k"], d["v"], d["slots"], kc, vc, stream=stream)
         decode(i)
 
@@ -663,6 +674,8 @@ def main():
         "decode_seqs_per_s": round(sh.num_seqs / (dec_avg_ms * 1e-3), 1),
         "step_seqs_per_s": round(sh.num_seqs / (ms_per_step * 1e-3), 1),
         "event_ms_per_step": round(step_gpu_ms, 4),
+        "step_launches": "copy_blocks (when pairs) + fused append/decode" if fused
+                         else "copy_blocks (when pairs) + paged_kv_write + decode",
         "decode_ms": round(dec_avg_ms, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -11,6 +11,7 @@
  *   pkv_copy_blocks             copy whole blocks (copy-on-write of shared blocks)
  *   pkv_swap_blocks             copy whole blocks between HBM and host memory
  *   pkv_paged_attention_decode  one-query-per-sequence attention through the table
+ *   pkv_paged_attention_decode_append  the same with the new token's K/V written in the launch
  *   pkv_paged_attention_prefill causal attention of several new tokens per sequence
  *   pkv_alloc_* / pkv_seq_*     free list, ref counts, lazy allocation, fork, CoW
  *
@@ -167,6 +168,29 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
                                int32_t num_q_heads, int32_t max_context_len, float scale,
                                int32_t partition_size, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/*
+ * Append + decode in one launch: for each sequence s with n = context_lens[s]
+ * >= 1, the new token's K/V rows k_new[s], v_new[s] ([num_seqs, Hkv, D],
+ * dtype) are written to the slot of position n - 1 (block
+ * block_tables[s][(n - 1) / B], offset (n - 1) % B), and the decode of
+ * pkv_paged_attention_decode runs over positions 0..n-1 with the appended row
+ * read from k_new / v_new.  Same results, bit for bit, as pkv_paged_kv_write of
+ * those rows followed by pkv_paged_attention_decode, with one launch fewer.
+ * The slot of position n - 1 must not be shared with another sequence (the
+ * allocator's copy-on-write guarantees this; run pkv_copy_blocks first).
+ * Sequences with n = 0 append nothing.  Runs the balanced split only: bf16
+ * caches and num_seqs <= 8191 (PKV_EUNSUPPORTED otherwise).  Workspace as for
+ * pkv_decode_workspace_bytes(..., PKV_PARTITION_AUTO).
+ * Errors: as pkv_paged_attention_decode.
+ */
+int pkv_paged_attention_decode_append(void* out, const void* q, const void* k_new,
+                                      const void* v_new, void* k_cache, void* v_cache,
+                                      const pkv_cache_desc* c, const int32_t* block_tables,
+                                      int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                      int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t max_context_len, float scale, void* workspace,
+                                      size_t workspace_bytes, void* stream);
 
 /*
  * Causal attention of several new tokens per sequence over the sequence's

@@ -26,6 +26,7 @@ from ._lib import (  # noqa: F401
     header_functions,
     lib,
     paged_attention_decode,
+    paged_attention_decode_append,
     paged_attention_prefill,
     paged_kv_write,
     swap_blocks,

@@ -62,6 +62,9 @@ _SIGS = {
     "pkv_decode_workspace_bytes": (_sz, [_P(CacheDesc), _i32, _i32, _i32, _i32]),
     "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _P(CacheDesc), _vp, _i32, _vp, _i32,
                                           _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
+    "pkv_paged_attention_decode_append": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _P(CacheDesc), _vp,
+                                                 _i32, _vp, _i32, _i32, _i32, _f32, _vp, _sz,
+                                                 _vp]),
     "pkv_paged_attention_prefill": (_i32, [_vp, _vp, _vp, _vp, _P(CacheDesc), _vp, _i32, _vp, _vp,
                                            _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
     "pkv_validate_prefill": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _P(CacheDesc)]),
@@ -229,6 +232,34 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S, Hq,
         int(max_context_len), float(scale), int(partition_size), _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+def paged_attention_decode_append(out, q, k_new, v_new, k_cache, v_cache, block_tables,
+                                  context_lens, scale: float, max_context_len: int,
+                                  workspace=None, stream=None) -> None:
+    """Write k_new / v_new [S, Hkv, D] at each sequence's last position and
+    decode, in one launch (the balanced split)."""
+    torch = _torch()
+    S, Hq, D = q.shape
+    if out.shape != q.shape or out.dtype != q.dtype or q.dtype != k_cache.dtype:
+        raise PagedKVError(PKV_EINVAL, "out/q/cache dtype or shape mismatch")
+    if k_new.shape != (S, k_cache.shape[1], D) or v_new.shape != k_new.shape \
+            or k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
+        raise PagedKVError(PKV_EINVAL, "k_new and v_new must be [S, Hkv, D] of the cache dtype")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise PagedKVError(PKV_EINVAL, "block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise PagedKVError(PKV_EINVAL, "block_tables must be [S, M] and context_lens [S]")
+    desc = cache_desc(k_cache)
+    if workspace is None and S:
+        need = decode_workspace_bytes(desc, S, Hq, max_context_len, PKV_PARTITION_AUTO)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pkv_paged_attention_decode_append(
+        _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+        ctypes.byref(desc), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S, Hq,
+        int(max_context_len), float(scale), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens,

@@ -406,15 +406,18 @@ struct KVTile {
 // that is not live, or whose block id is outside the pool, reads `safe` (a
 // small in-bounds row) instead, and its V is zeroed when it is used.  The
 // loads are never predicated, so the compiler can count them in flight.
+// A non-null k_row / v_row replaces the cache as the source of the row (the
+// appended token of the fused append + decode, read from its input).
 template <int D, int B>
 __device__ inline void load_kv(KVTile<D>& x, const uint16_t* __restrict__ k_cache,
                                const uint16_t* __restrict__ v_cache, const uint16_t* safe,
                                bool live, int phys, int tok, int g, int num_kv_heads,
-                               int num_blocks, int grp) {
+                               int num_blocks, int grp, const uint16_t* k_row = nullptr,
+                               const uint16_t* v_row = nullptr) {
   x.ok = live && phys >= 0 && phys < num_blocks;
   const int64_t off = ((int64_t)phys * num_kv_heads + g) * (B * D) + (int64_t)(tok % B) * D + 8 * grp;
-  const uint16_t* kp = x.ok ? k_cache + off : safe;
-  const uint16_t* vp = x.ok ? v_cache + off : safe;
+  const uint16_t* kp = x.ok ? (k_row ? k_row : k_cache + off) : safe;
+  const uint16_t* vp = x.ok ? (v_row ? v_row : v_cache + off) : safe;
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) {
     x.k[kk] = *reinterpret_cast<const uint4*>(kp + 32 * kk);
@@ -671,14 +674,15 @@ __device__ inline int worker_of(int64_t u, int64_t total, int32_t num_workers) {
   return (int)(((u + 1) * num_workers - 1) / total);
 }
 
-template <int D, int B, int G>
+template <int D, int B, int G, bool kAppend>
 __global__ __launch_bounds__(kThreads) void decode_balanced_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     int32_t table_width, const int32_t* __restrict__ context_lens, uint16_t* __restrict__ out,
     int2* __restrict__ meta, float* __restrict__ part_ml, float* __restrict__ part_o,
     int32_t num_seqs, int32_t num_kv_heads, int32_t num_blocks, int32_t max_context_len,
-    int32_t num_workers, float qscale) {
+    int32_t num_workers, float qscale, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, uint16_t* k_dst, uint16_t* v_dst) {
   constexpr int DT = D / 16;
   extern __shared__ int32_t sm_dyn[];
   int32_t* sm_c = sm_dyn;                 // [num_seqs + 1] tiles of one KV head before sequence s
@@ -727,6 +731,29 @@ __global__ __launch_bounds__(kThreads) void decode_balanced_kernel(
     for (int e = threadIdx.x; e < hq * D; e += kThreads) out[(int64_t)i * hq * D + e] = 0;
     for (int g = threadIdx.x; g < num_kv_heads; g += kThreads)
       meta[(int64_t)i * num_kv_heads + g] = make_int2(-1, -1);
+  }
+  if constexpr (kAppend) {
+    // The appended rows go to their slots here, before any worker starts, so
+    // no store sits in the workers' pipelined loop; the workers read those
+    // rows from k_new / v_new, never from the slots written here.
+    constexpr int kChunks = D / 8;
+    const int per_seq = 2 * num_kv_heads * kChunks;  // K and V, 16-byte pieces
+    for (int i = blockIdx.x; i < num_seqs; i += gridDim.x) {
+      const int t = sm_n[i] - 1;
+      if (t < 0) continue;
+      const int phys = block_tables[(int64_t)i * table_width + t / B];
+      if (phys < 0 || phys >= num_blocks) continue;
+      for (int e = threadIdx.x; e < per_seq; e += kThreads) {
+        const int which = e / (num_kv_heads * kChunks);
+        const int r = e - which * num_kv_heads * kChunks;
+        const int g = r / kChunks;
+        const int c = r - g * kChunks;
+        const int64_t src = ((int64_t)i * num_kv_heads + g) * D + 8 * c;
+        const int64_t dst = (((int64_t)phys * num_kv_heads + g) * B + t % B) * D + 8 * c;
+        const uint4 x = *reinterpret_cast<const uint4*>((which ? v_new : k_new) + src);
+        *reinterpret_cast<uint4*>((which ? v_dst : k_dst) + dst) = x;
+      }
+    }
   }
   const int64_t total = (int64_t)num_kv_heads * sm_c[num_seqs];
   // With fewer tiles than workers only the first `total` workers take one
@@ -787,10 +814,20 @@ __global__ __launch_bounds__(kThreads) void decode_balanced_kernel(
     return block_tables[(int64_t)x.s * table_width + t / B];
   };
   const uint16_t* safe = q + 8 * grp;
+  // With kAppend the row of position n - 1 (the token appended this step)
+  // comes from k_new / v_new [num_seqs, Hkv, D] instead of the cache, and
+  // step() stores it into the cache slot: the same bits either way.
   auto load_tile = [&](const Pos& x, int phys, bool live, KVTile<D>& kv) {
     const int t = ptile(x) * kTile + col;
+    const uint16_t* kr = nullptr;
+    const uint16_t* vr = nullptr;
+    if constexpr (kAppend) {
+      const int64_t nrow = ((int64_t)x.s * num_kv_heads + x.g) * D + 8 * grp;
+      kr = t == x.n - 1 ? k_new + nrow : nullptr;
+      vr = t == x.n - 1 ? v_new + nrow : nullptr;
+    }
     load_kv<D, B>(kv, k_cache, v_cache, safe, live && t < x.n, phys, t, x.g, num_kv_heads,
-                  num_blocks, grp);
+                  num_blocks, grp, kr, vr);
   };
 
   MfmaAttn<D, G> at;
@@ -1038,6 +1075,8 @@ struct LaunchArgs {
   int32_t num_blocks;
   int32_t max_context_len;
   int32_t num_q_heads;
+  const void* k_new;  // non-null: fused append (balanced split only)
+  const void* v_new;
   Plan plan;
   float qscale;
   int2* meta;
@@ -1057,12 +1096,23 @@ int launch(const LaunchArgs& a) {
   if constexpr (E::bytes == 2) {
     if (a.plan.balanced) {
       const size_t lds = (size_t)(2 * a.num_seqs + 1) * sizeof(int32_t);
-      hipLaunchKernelGGL((decode_balanced_kernel<D, B, G>), dim3((uint32_t)(a.plan.workers / kWaves)),
-                         dim3(kThreads), lds, a.stream, (const uint16_t*)a.q,
-                         (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.block_tables,
-                         a.width, a.context_lens, (uint16_t*)a.out, a.meta, a.part_ml, a.part_o,
-                         a.num_seqs, a.num_kv_heads, a.num_blocks, a.max_context_len,
-                         a.plan.workers, a.qscale);
+      if (a.k_new)
+        hipLaunchKernelGGL((decode_balanced_kernel<D, B, G, true>),
+                           dim3((uint32_t)(a.plan.workers / kWaves)), dim3(kThreads), lds,
+                           a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
+                           (const uint16_t*)a.v_cache, a.block_tables, a.width, a.context_lens,
+                           (uint16_t*)a.out, a.meta, a.part_ml, a.part_o, a.num_seqs,
+                           a.num_kv_heads, a.num_blocks, a.max_context_len, a.plan.workers,
+                           a.qscale, (const uint16_t*)a.k_new, (const uint16_t*)a.v_new,
+                           (uint16_t*)a.k_cache, (uint16_t*)a.v_cache);
+      else
+        hipLaunchKernelGGL((decode_balanced_kernel<D, B, G, false>),
+                           dim3((uint32_t)(a.plan.workers / kWaves)), dim3(kThreads), lds,
+                           a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
+                           (const uint16_t*)a.v_cache, a.block_tables, a.width, a.context_lens,
+                           (uint16_t*)a.out, a.meta, a.part_ml, a.part_o, a.num_seqs,
+                           a.num_kv_heads, a.num_blocks, a.max_context_len, a.plan.workers,
+                           a.qscale, nullptr, nullptr, nullptr, nullptr);
       int rc = check_launch("decode_balanced");
       if (rc) return rc;
       const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * G;
@@ -1164,15 +1214,14 @@ extern "C" size_t pkv_decode_workspace_bytes(const pkv_cache_desc* c, int32_t nu
   return pl.bytes;
 }
 
-extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
-                                          const void* v_cache, const pkv_cache_desc* c,
-                                          const int32_t* block_tables,
-                                          int32_t max_blocks_per_seq,
-                                          const int32_t* context_lens, int32_t num_seqs,
-                                          int32_t num_q_heads, int32_t max_context_len,
-                                          float scale, int32_t partition_size, void* workspace,
-                                          size_t workspace_bytes, void* stream) {
-  pkv__clear_error();
+namespace {
+
+int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
+                const void* k_cache, const void* v_cache, const pkv_cache_desc* c,
+                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
+                size_t workspace_bytes, void* stream) {
   int rc = check_sizes(c, num_seqs, num_q_heads, max_context_len, partition_size);
   if (rc) return rc;
   if (max_blocks_per_seq < 0 || (int64_t)max_blocks_per_seq * c->block_size < max_context_len)
@@ -1189,6 +1238,15 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
   Plan pl;
   rc = make_plan(c, num_seqs, num_q_heads, max_context_len, partition_size, &pl);
   if (rc) return rc;
+  if (k_new) {
+    if (!v_new) return pkv__fail(PKV_EINVAL, "v_new is NULL");
+    if (!pl.balanced)
+      return pkv__fail(PKV_EUNSUPPORTED,
+                       "the fused append runs in the balanced split only (bf16 caches, "
+                       "PKV_PARTITION_AUTO, num_seqs <= %d)", kMaxSeqsBalanced);
+    if (!aligned16(k_new) || !aligned16(v_new))
+      return pkv__fail(PKV_EINVAL, "k_new and v_new must be 16-byte aligned");
+  }
   if (workspace_bytes < pl.bytes || (pl.bytes && !workspace))
     return pkv__fail(PKV_EINVAL, "workspace of %zu bytes is smaller than the %zu needed",
                      workspace_bytes, pl.bytes);
@@ -1208,6 +1266,8 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
   a.num_blocks = c->num_blocks;
   a.max_context_len = max_context_len;
   a.num_q_heads = num_q_heads;
+  a.k_new = k_new;
+  a.v_new = v_new;
   a.plan = pl;
   a.qscale = scale * kLog2e;
   char* ws = (char*)workspace;
@@ -1218,4 +1278,32 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
   const int G = num_q_heads / c->num_kv_heads;
   if (c->dtype == PKV_BF16) return dispatch_d<BF16>(a, c->head_dim, c->block_size, G);
   return dispatch_d<F32>(a, c->head_dim, c->block_size, G);
+}
+
+}  // namespace
+
+extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
+                                          const void* v_cache, const pkv_cache_desc* c,
+                                          const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens, int32_t num_seqs,
+                                          int32_t num_q_heads, int32_t max_context_len,
+                                          float scale, int32_t partition_size, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  pkv__clear_error();
+  return decode_impl(out, q, nullptr, nullptr, k_cache, v_cache, c, block_tables,
+                     max_blocks_per_seq, context_lens, num_seqs, num_q_heads, max_context_len,
+                     scale, partition_size, workspace, workspace_bytes, stream);
+}
+
+extern "C" int pkv_paged_attention_decode_append(
+    void* out, const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+    const pkv_cache_desc* c, const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+    float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  pkv__clear_error();
+  if (!k_new || !v_new) return pkv__fail(PKV_EINVAL, "NULL k_new or v_new");
+  return decode_impl(out, q, k_new, v_new, k_cache, v_cache, c, block_tables, max_blocks_per_seq,
+                     context_lens, num_seqs, num_q_heads, max_context_len, scale,
+                     PKV_PARTITION_AUTO, workspace, workspace_bytes, stream);
 }
