@@ -101,3 +101,40 @@ def test_fp32_caches_are_not_built_for_the_fused_path():
     with pytest.raises(pkv.PagedKVError) as ei:
         pkv.paged_attention_decode_append(q.clone(), q, nk, nk, kc, kc, t, c, 1.0, 1)
     assert ei.value.code == pkv.PKV_EUNSUPPORTED
+
+
+def test_empty_sequence_appends_nothing_and_copy_first():
+    """A sequence of length 0 writes nothing; a step whose append needed a
+    copy-on-write runs copy_blocks first, then the fused call."""
+    rng = np.random.default_rng(12)
+    Hq, Hkv, D, B = 8, 2, 128, 16
+    nb = 40
+    m = BlockAllocatorModel(nb, B, rng.permutation(nb).astype(np.int32))
+    kc = datagen.normal(rng, (nb, Hkv, B, D), "bf16")
+    vc = datagen.normal(rng, (nb, Hkv, B, D), "bf16")
+    slots = m.add(0, 21)
+    kc, vc = paged_kv_write(datagen.normal(rng, (21, Hkv, D), "bf16"),
+                            datagen.normal(rng, (21, Hkv, D), "bf16"), slots, kc, vc)
+    m.fork(0, 1)
+    m.add(2, 0)                                   # stays empty
+    slots, pairs = m.step([0, 1])
+    assert len(pairs) == 1                        # sequence 0 copies the shared partial block
+    tables, ctx = m.build_tables([0, 1, 2], 2)
+    tables, ctx = np.array(tables, np.int32), np.array(ctx, np.int32)
+    nk = datagen.normal(rng, (3, Hkv, D), "bf16")
+    nv = datagen.normal(rng, (3, Hkv, D), "bf16")
+    q = datagen.normal(rng, (3, Hq, D), "bf16")
+    dk, dv = dev(kc), dev(vc)
+    pkv.copy_blocks(dk, dv, dev(np.array(pairs, np.int32)))
+    out = torch.empty_like(dev(q))
+    pkv.paged_attention_decode_append(out, dev(q), dev(nk), dev(nv), dk, dv, dev(tables), dev(ctx),
+                                      0.09, int(ctx.max()))
+    torch.cuda.synchronize()
+    from oracle import copy_blocks as o_copy
+    ek, ev = o_copy(kc, vc, pairs)
+    ek, ev = paged_kv_write(nk[:2], nv[:2], np.array(slots, np.int64), ek, ev)
+    assert np.array_equal(host(dk), ek) and np.array_equal(host(dv), ev)
+    ref = paged_attention_decode(q, ek, ev, tables, ctx, 0.09, "bf16")
+    got = host(out)
+    check_close(got, ref, "bf16")
+    assert not got[2].any(), "an empty sequence decodes to zeros"

@@ -166,3 +166,30 @@ def test_chunked_prefill_workload_full_size():
                                   sh.scale, "bf16", seqs=sample)
     rows = np.concatenate([np.arange(w.qsl[s], w.qsl[s + 1]) for s in sample])
     print("prefill full max_abs/max_rel", check_close(got[rows], ref[rows], "bf16"))
+
+
+def test_long_prefix_and_many_single_token_sequences():
+    """A 30000-token cached prefix with a 64-token chunk, next to 40 sequences
+    with one new token each: sampled rows of the long one, all rows of a few
+    short ones."""
+    rng = np.random.default_rng(45)
+    lens = [30064] + [int(x) for x in rng.integers(1, 300, size=40)]
+    news = [64] + [1] * 40
+    print("prefill long prefix", flush=True)
+    q, kc, vc, tables, ctx, qsl = _case(rng, lens, news, 32, 8, 128, 16, extra_blocks=3)
+    got = _run(q, kc, vc, tables, ctx, qsl, 0.088)
+    sample = [0, 1, 2, 40]
+    ref = paged_attention_prefill(q, kc, vc, tables, ctx, qsl, 0.088, "bf16", seqs=sample,
+                                  heads=[0, 5, 31])
+    rows = np.concatenate([np.arange(qsl[s], qsl[s + 1]) for s in sample])
+    check_close(got[rows][:, [0, 5, 31]], ref[rows][:, [0, 5, 31]], "bf16")
+
+
+def test_empty_launches_do_nothing():
+    q = torch.zeros((0, 8, 128), dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros((4, 2, 16, 128), dtype=torch.bfloat16, device="cuda")
+    t = torch.zeros((0, 1), dtype=torch.int32, device="cuda")
+    c = torch.zeros((0,), dtype=torch.int32, device="cuda")
+    qsl = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    pkv.paged_attention_prefill(q.clone(), q, kc, kc, t, c, qsl, 1.0, 0, 0)
+    torch.cuda.synchronize()
