@@ -193,3 +193,18 @@ def test_empty_launches_do_nothing():
     qsl = torch.zeros((1,), dtype=torch.int32, device="cuda")
     pkv.paged_attention_prefill(q.clone(), q, kc, kc, t, c, qsl, 1.0, 0, 0)
     torch.cuda.synchronize()
+
+
+def test_values_beyond_fp16_take_the_bf16_path():
+    """V rows with magnitudes past fp16's range (bf16 holds them) must still
+    match the oracle: their tiles take the bf16 product."""
+    rng = np.random.default_rng(46)
+    lens, news = [200, 90], [70, 90]
+    q, kc, vc, tables, ctx, qsl = _case(rng, lens, news, 32, 8, 128, 16)
+    big = datagen.bf16_from_f32(np.array([3.0e5, -1.2e6, 7.0e4], np.float32))
+    # a few live slots of sequence 0 get huge V entries
+    for t, val in zip((5, 77, 150), big):
+        vc[tables[0][t // 16], 3, t % 16, 11] = val
+    got = _run(q, kc, vc, tables, ctx, qsl, 1.0 / math.sqrt(128))
+    ref = paged_attention_prefill(q, kc, vc, tables, ctx, qsl, 1.0 / math.sqrt(128), "bf16")
+    check_close(got, ref, "bf16")
