@@ -295,13 +295,23 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(
     for (int h = 0; h < 2; ++h) {
       sc[0][h] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
       sc[1][h] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    // K fragments in order j = h KK + kk, each read two steps before its
+    // two MFMAs so the LDS latency overlaps the products of the previous ones.
+    auto kread = [&](int j) {
+      const int h = j / KK, kk = j % KK;
+      return *reinterpret_cast<const uint4*>(lk + (16 * h + col) * Pitch<D>::kElems + 32 * kk +
+                                             8 * grp);
+    };
+    uint4 kf0 = kread(0), kf1 = kread(1);
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const uint4 a = *reinterpret_cast<const uint4*>(lk + (16 * h + col) * Pitch<D>::kElems +
-                                                        32 * kk + 8 * grp);
-        sc[0][h] = mfma16x16x32(a, qv[0][kk], sc[0][h]);
-        sc[1][h] = mfma16x16x32(a, qv[1][kk], sc[1][h]);
-      }
+    for (int j = 0; j < 2 * KK; ++j) {
+      const uint4 a = kf0;
+      kf0 = kf1;
+      if (j + 2 < 2 * KK) kf1 = kread(j + 2);
+      const int h = j / KK;
+      sc[0][h] = mfma16x16x32(a, qv[0][j % KK], sc[0][h]);
+      sc[1][h] = mfma16x16x32(a, qv[1][j % KK], sc[1][h]);
     }
 
     // Online softmax of each row; P^T operands (hi and lo parts) in the S^T
@@ -354,15 +364,20 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(
     // 16 + 4 grp + k, the order of P^T's k-slots.
     const int key_a = 4 * grp + (col >> 2);
     const int dofs = 4 * (col & 3);
-#pragma unroll
-    for (int t = 0; t < DT; ++t) {
+    auto vread = [&](int t) {
       const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4_t*)(lv + key_a * Pitch<D>::kElems + 16 * t + dofs));
       const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4_t*)(lv + (key_a + 16) * Pitch<D>::kElems + 16 * t + dofs));
       const uint2 a0 = __builtin_bit_cast(uint2, v0);
       const uint2 a1 = __builtin_bit_cast(uint2, v1);
-      const uint4 a = make_uint4(a0.x, a0.y, a1.x, a1.y);
+      return make_uint4(a0.x, a0.y, a1.x, a1.y);
+    };
+    uint4 an = vread(0);
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      const uint4 a = an;
+      if (t + 1 < DT) an = vread(t + 1);
       o[0][t] = mfma16x16x32(a, pb[0], o[0][t]);
       o[1][t] = mfma16x16x32(a, pb[1], o[1][t]);
       o[0][t] = mfma16x16x32(a, pl[0], o[0][t]);
