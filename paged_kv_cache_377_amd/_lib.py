@@ -143,11 +143,25 @@ def _dtype_code(t) -> int:
     raise PagedKVError(PKV_EINVAL, f"unsupported dtype {t.dtype}")
 
 
-def _ptr(t) -> Optional[int]:
+def _ptr(t, host_ok: bool = False) -> Optional[int]:
+    """Address of a contiguous tensor that the kernels can reach: memory of
+    the current GPU, or (host_ok) pinned host memory.  Anything else would hand
+    a kernel an address it cannot access, so it is refused here.  Empty
+    tensors are passed through (nothing is read from them)."""
     if t is None:
         return None
     if not t.is_contiguous():
         raise PagedKVError(PKV_EINVAL, "tensors must be contiguous")
+    if t.numel():
+        if t.is_cuda:
+            cur = _torch().cuda.current_device()
+            if t.device.index != cur:
+                raise PagedKVError(PKV_EINVAL,
+                                   f"tensor on {t.device}, but the current device is cuda:{cur}")
+        elif not (host_ok and t.is_pinned()):
+            raise PagedKVError(PKV_EINVAL, "tensor must be in GPU memory"
+                               + (" or pinned host memory" if host_ok else "")
+                               + f", got {t.device}" + (" (not pinned)" if host_ok else ""))
     return t.data_ptr()
 
 
@@ -296,8 +310,9 @@ def swap_blocks(dst_k, dst_v, src_k, src_v, pairs, stream=None) -> None:
     if dst_k.shape[1:] != src_k.shape[1:] or dst_k.dtype != src_k.dtype:
         raise PagedKVError(PKV_EINVAL, "pools differ in block shape or dtype")
     desc = cache_desc(dst_k)
-    _check(lib().pkv_swap_blocks(_ptr(dst_k), _ptr(dst_v), dst_k.shape[0], _ptr(src_k), _ptr(src_v),
-                                 src_k.shape[0], ctypes.byref(desc), _ptr(pairs),
+    _check(lib().pkv_swap_blocks(_ptr(dst_k, True), _ptr(dst_v, True), dst_k.shape[0],
+                                 _ptr(src_k, True), _ptr(src_v, True),
+                                 src_k.shape[0], ctypes.byref(desc), _ptr(pairs, True),
                                  pairs.shape[0] if pairs.numel() else 0, _stream(stream)))
 
 
