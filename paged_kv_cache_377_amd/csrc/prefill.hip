@@ -197,6 +197,122 @@ __device__ inline void stage_store(const Stage<D>& st, uint16_t* lk, uint16_t* l
   }
 }
 
+// ------------------------------------------------------- launch order
+//
+// A workgroup's run time is proportional to its number of key tiles, which
+// depends on the sequence's cached prefix, known only on the device.  The
+// workgroups are therefore handed their (sequence, q-tile) items longest
+// first: workgroup b takes the item of rank b / Hkv in the order of key-tile
+// count descending, ties by item index (s tps + qt), items with nothing to
+// do last.  Every workgroup computes the rank selection itself from
+// context_lens and query_start_loc: a histogram of the counts in LDS, the
+// bin of the rank, then the item inside the bin.  Without it the heavy
+// q-tiles of long-prefix sequences could start last and run alone at the
+// end of the launch.
+
+constexpr int kOrderBins = 4096;       // histogram bins (counts above are coarsened)
+constexpr int kOrderMaxItems = 65536;  // beyond: plain order (q-tiles heaviest first)
+
+// Exclusive prefix sum over the workgroup's threads (thread order); also
+// returns the total.  Uses `tmp` [kWaves] of LDS; ends with a barrier.
+__device__ inline int block_exclusive_scan(int v, int* tmp, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) tmp[wave] = x;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int t = tmp[w];
+    before += w < wave ? t : 0;
+    total += t;
+  }
+  __syncthreads();
+  return before + x - v;
+}
+
+// Key of item i = s tps + qt: key tiles + 1, or 0 when the q-tile holds no
+// new token (the same count the kernel's loop runs).
+template <int kTokens>
+__device__ inline int item_key(int i, int tiles_per_seq, const int32_t* __restrict__ context_lens,
+                               const int32_t* __restrict__ query_start_loc, int max_context_len) {
+  const int s = i / tiles_per_seq, qt = i - s * tiles_per_seq;
+  const int nnew = query_start_loc[s + 1] - query_start_loc[s];
+  const int j0 = qt * kTokens;
+  if (j0 >= nnew) return 0;
+  const int n = min(context_lens[s], max_context_len);
+  const int pmax = n - nnew + min(j0 + kTokens, nnew) - 1;
+  return (pmax >= 0 ? (pmax + kKeys) / kKeys : 0) + 1;
+}
+
+// The item of rank `rank` (see above); `hist` is kOrderBins ints of LDS and
+// `tmp` kWaves + 2 ints.  All threads of the workgroup call it.
+template <int kTokens>
+__device__ int item_of_rank(int rank, int items, int tiles_per_seq,
+                            const int32_t* __restrict__ context_lens,
+                            const int32_t* __restrict__ query_start_loc, int max_context_len,
+                            int* hist, int* tmp) {
+  // keys lie in [0, max_context_len / kKeys + 2]; coarsen them to the bins
+  const int max_key = max_context_len / kKeys + 2;
+  int shift = 0;
+  while ((max_key >> shift) >= kOrderBins) ++shift;
+  for (int b = threadIdx.x; b < kOrderBins; b += kThreads) hist[b] = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < items; i += kThreads)
+    atomicAdd(&hist[item_key<kTokens>(i, tiles_per_seq, context_lens, query_start_loc,
+                                      max_context_len) >> shift], 1);
+  __syncthreads();
+  // bin of the rank: bins from the highest down, kOrderBins / kThreads per thread
+  constexpr int kPer = kOrderBins / kThreads;
+  const int top = kOrderBins - 1 - (int)threadIdx.x * kPer;  // this thread's bins top .. top - kPer + 1
+  int mine = 0;
+  for (int k = 0; k < kPer; ++k) mine += hist[top - k];
+  int total;
+  int above = block_exclusive_scan(mine, tmp, total);  // items in higher bins
+  if (rank >= above && rank < above + mine) {
+    for (int k = 0; k < kPer; ++k) {
+      const int c = hist[top - k];
+      if (rank < above + c) {
+        tmp[kWaves] = top - k;
+        tmp[kWaves + 1] = rank - above;  // position inside the bin
+        break;
+      }
+      above += c;
+    }
+  }
+  __syncthreads();
+  const int bin = tmp[kWaves], pos = tmp[kWaves + 1];
+  // the pos-th item (index order) of that bin: contiguous item ranges per thread
+  const int per = (items + kThreads - 1) / kThreads;
+  const int i0 = min(items, (int)threadIdx.x * per), i1 = min(items, i0 + per);
+  int cnt = 0;
+  for (int i = i0; i < i1; ++i)
+    cnt += (item_key<kTokens>(i, tiles_per_seq, context_lens, query_start_loc, max_context_len) >>
+            shift) == bin;
+  const int before = block_exclusive_scan(cnt, tmp, total);
+  if (pos >= before && pos < before + cnt) {
+    int k = before;
+    for (int i = i0; i < i1; ++i) {
+      if ((item_key<kTokens>(i, tiles_per_seq, context_lens, query_start_loc, max_context_len) >>
+           shift) != bin)
+        continue;
+      if (k == pos) {
+        tmp[kWaves + 2] = i;
+        break;
+      }
+      ++k;
+    }
+  }
+  __syncthreads();
+  return tmp[kWaves + 2];
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
@@ -214,11 +330,26 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(
 
   // Heaviest tiles (last new tokens, most keys) first; the workgroups of one
   // (sequence, KV head) are num_seqs * num_kv_heads apart in launch order.
+  // Workgroup b serves KV head b % Hkv (consecutive workgroups go to
+  // different XCDs, so each XCD's L2 keeps the K/V of its heads) and the
+  // item of rank b / Hkv, longest first.
   const int bid = blockIdx.x;
   const int g = bid % num_kv_heads;
   const int rest = bid / num_kv_heads;
-  const int s = rest % num_seqs;
-  const int qt = tiles_per_seq - 1 - rest / num_seqs;
+  const int items = num_seqs * tiles_per_seq;
+  int s, qt;
+  if (items <= kOrderMaxItems) {
+    __shared__ int sm_tmp[kWaves + 3];
+    // the histogram lives in the staging buffers, unused until the pipeline starts
+    const int it = item_of_rank<kTokens>(rest, items, tiles_per_seq, context_lens,
+                                         query_start_loc, max_context_len,
+                                         reinterpret_cast<int*>(&lds[0][0][0]), sm_tmp);
+    s = it / tiles_per_seq;
+    qt = it - s * tiles_per_seq;
+  } else {
+    s = rest % num_seqs;
+    qt = tiles_per_seq - 1 - rest / num_seqs;
+  }
 
   const int q0 = query_start_loc[s];
   const int q1 = query_start_loc[s + 1];

@@ -196,8 +196,8 @@ def test_empty_launches_do_nothing():
 
 
 def test_values_beyond_fp16_take_the_bf16_path():
-    """V rows with magnitudes past fp16's range (bf16 holds them) must still
-    match the oracle: their tiles take the bf16 product."""
+    """V entries far past fp16's range (bf16 holds them) still match the
+    oracle: V enters the P V product in bf16, whatever its magnitude."""
     rng = np.random.default_rng(46)
     lens, news = [200, 90], [70, 90]
     q, kc, vc, tables, ctx, qsl = _case(rng, lens, news, 32, 8, 128, 16)
@@ -208,3 +208,37 @@ def test_values_beyond_fp16_take_the_bf16_path():
     got = _run(q, kc, vc, tables, ctx, qsl, 1.0 / math.sqrt(128))
     ref = paged_attention_prefill(q, kc, vc, tables, ctx, qsl, 1.0 / math.sqrt(128), "bf16")
     check_close(got, ref, "bf16")
+
+
+def test_launch_order_with_coarsened_bins():
+    """A 140000-token context puts the key-tile counts past the order's 4096
+    histogram bins (two counts per bin): the items are still all served once,
+    beside a fresh prompt and a one-token step."""
+    rng = np.random.default_rng(47)
+    lens, news = [140000, 100, 5000], [40, 100, 1]
+    print("prefill coarsened order", flush=True)
+    q, kc, vc, tables, ctx, qsl = _case(rng, lens, news, 4, 1, 128, 16, extra_blocks=3)
+    got = _run(q, kc, vc, tables, ctx, qsl, 0.088)
+    ref = paged_attention_prefill(q, kc, vc, tables, ctx, qsl, 0.088, "bf16")
+    check_close(got, ref, "bf16")
+
+
+def test_launch_order_past_the_item_limit():
+    """More than 65536 (sequence, q-tile) items: the launch falls back to the
+    plain order.  4096 sequences, most with one new token, some with up to 140
+    (18 q-tiles of 8 tokens at 16 query heads per KV head); sampled sequences."""
+    rng = np.random.default_rng(48)
+    S = 4096
+    news = np.ones(S, np.int64)
+    big = rng.choice(S, 12, replace=False)
+    news[big] = rng.integers(60, 141, size=12)
+    news[big[0]] = 140
+    lens = news + rng.integers(0, 50, size=S)
+    print("prefill plain order past the item limit", flush=True)
+    q, kc, vc, tables, ctx, qsl = _case(rng, lens.tolist(), news.tolist(), 16, 1, 64, 16,
+                                        extra_blocks=3)
+    got = _run(q, kc, vc, tables, ctx, qsl, 0.125)
+    sample = sorted(set(big.tolist()) | {0, S - 1} | set(rng.choice(S, 20, replace=False).tolist()))
+    ref = paged_attention_prefill(q, kc, vc, tables, ctx, qsl, 0.125, "bf16", seqs=sample)
+    rows = np.concatenate([np.arange(qsl[s], qsl[s + 1]) for s in sample])
+    check_close(got[rows], ref[rows], "bf16")
