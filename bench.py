@@ -333,11 +333,22 @@ def cpu_baseline(wl: Workload, min_s: float = 10.0, max_s: float = 20.0):
                 continue
             break
     dt = time.perf_counter() - t0
+    # the oracle's allocator on the same step as the library's (allocator_us_per_step)
+    need = sum(-(-(int(n) + 50) // sh.block_size) for n in st["ctx"]) + sh.num_seqs
+    m = oracle.BlockAllocatorModel(need, sh.block_size)
+    for s in range(sh.num_seqs):
+        m.add(s, int(st["ctx"][s]) - 1)
+    ta = time.perf_counter()
+    for _ in range(20):
+        m.step(wl.seq_ids)
+        m.build_tables(wl.seq_ids, wl.width + 8)
+    alloc_us = (time.perf_counter() - ta) / 20 * 1e6
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"fp64 decode of step 0's batch ({sh.num_seqs} sequences, all {sh.num_q_heads} "
                       f"heads) repeated: {done} sequence decodes ({reps} whole batches) in {dt:.1f} s, "
                       f"numpy/BLAS limited to 1 thread",
-            "seqs_per_s": done / dt}
+            "seqs_per_s": done / dt,
+            "allocator_us_per_step": round(alloc_us, 1)}
 
 
 def copy_probe(mib: int, reps: int) -> None:
