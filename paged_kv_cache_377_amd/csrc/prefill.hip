@@ -210,8 +210,8 @@ __device__ inline void stage_store(const Stage<D>& st, uint16_t* lk, uint16_t* l
 // q-tiles of long-prefix sequences could start last and run alone at the
 // end of the launch.
 
-constexpr int kOrderBins = 4096;       // histogram bins (counts above are coarsened)
-constexpr int kOrderMaxItems = 65536;  // beyond: plain order (q-tiles heaviest first)
+constexpr int kOrderBins = 4096;     // histogram bins (counts above are coarsened)
+constexpr int kOrderMaxItems = 512;  // beyond: plain order (q-tiles heaviest first)
 
 // Exclusive prefix sum over the workgroup's threads (thread order); also
 // returns the total.  Uses `tmp` [kWaves] of LDS; ends with a barrier.
@@ -251,22 +251,29 @@ __device__ inline int item_key(int i, int tiles_per_seq, const int32_t* __restri
   return (pmax >= 0 ? (pmax + kKeys) / kKeys : 0) + 1;
 }
 
-// The item of rank `rank` (see above); `hist` is kOrderBins ints of LDS and
-// `tmp` kWaves + 2 ints.  All threads of the workgroup call it.
+// The item of rank `rank` (see above); `hist` is kOrderBins + kOrderMaxItems
+// ints of LDS (the histogram, then each item's key), `tmp` kWaves + 3 ints.
+// All threads of the workgroup call it; items <= kOrderMaxItems.  Its cost
+// (two item keys per thread, four barriers and two scans) is what limits the
+// item count: every workgroup repeats it.
 template <int kTokens>
 __device__ int item_of_rank(int rank, int items, int tiles_per_seq,
                             const int32_t* __restrict__ context_lens,
                             const int32_t* __restrict__ query_start_loc, int max_context_len,
                             int* hist, int* tmp) {
+  int* keys = hist + kOrderBins;
   // keys lie in [0, max_context_len / kKeys + 2]; coarsen them to the bins
   const int max_key = max_context_len / kKeys + 2;
   int shift = 0;
   while ((max_key >> shift) >= kOrderBins) ++shift;
   for (int b = threadIdx.x; b < kOrderBins; b += kThreads) hist[b] = 0;
   __syncthreads();
-  for (int i = threadIdx.x; i < items; i += kThreads)
-    atomicAdd(&hist[item_key<kTokens>(i, tiles_per_seq, context_lens, query_start_loc,
-                                      max_context_len) >> shift], 1);
+  for (int i = threadIdx.x; i < items; i += kThreads) {
+    const int k = item_key<kTokens>(i, tiles_per_seq, context_lens, query_start_loc,
+                                    max_context_len) >> shift;
+    keys[i] = k;
+    atomicAdd(&hist[k], 1);
+  }
   __syncthreads();
   // bin of the rank: bins from the highest down, kOrderBins / kThreads per thread
   constexpr int kPer = kOrderBins / kThreads;
@@ -292,16 +299,12 @@ __device__ int item_of_rank(int rank, int items, int tiles_per_seq,
   const int per = (items + kThreads - 1) / kThreads;
   const int i0 = min(items, (int)threadIdx.x * per), i1 = min(items, i0 + per);
   int cnt = 0;
-  for (int i = i0; i < i1; ++i)
-    cnt += (item_key<kTokens>(i, tiles_per_seq, context_lens, query_start_loc, max_context_len) >>
-            shift) == bin;
+  for (int i = i0; i < i1; ++i) cnt += keys[i] == bin;
   const int before = block_exclusive_scan(cnt, tmp, total);
   if (pos >= before && pos < before + cnt) {
     int k = before;
     for (int i = i0; i < i1; ++i) {
-      if ((item_key<kTokens>(i, tiles_per_seq, context_lens, query_start_loc, max_context_len) >>
-           shift) != bin)
-        continue;
+      if (keys[i] != bin) continue;
       if (k == pos) {
         tmp[kWaves + 2] = i;
         break;
@@ -338,9 +341,11 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(
   const int rest = bid / num_kv_heads;
   const int items = num_seqs * tiles_per_seq;
   int s, qt;
+  static_assert(sizeof(lds) >= (kOrderBins + kOrderMaxItems) * sizeof(int), "order scratch");
   if (items <= kOrderMaxItems) {
     __shared__ int sm_tmp[kWaves + 3];
-    // the histogram lives in the staging buffers, unused until the pipeline starts
+    // the histogram and keys live in the staging buffers, unused until the
+    // pipeline starts (4608 ints; the smallest staging area holds 4608)
     const int it = item_of_rank<kTokens>(rest, items, tiles_per_seq, context_lens,
                                          query_start_loc, max_context_len,
                                          reinterpret_cast<int*>(&lds[0][0][0]), sm_tmp);
