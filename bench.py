@@ -77,8 +77,11 @@ def parse():
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--partition-size", type=int, default=-1,
                     help="-1: balanced split (default); > 0: split-context partitions; 0: no split")
-    ap.add_argument("--replicas", type=int, default=1,
-                    help="rotate over R copies of the KV pool (step i uses copy i %% R)")
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="rotate over R copies of the KV pool (step i uses copy i %% R); 0 (default): "
+                         "enough copies that a step never finds the previous steps' K/V in the "
+                         "GPU's 256 MiB Infinity Cache, as in a model whose other layers' caches "
+                         "are read between two steps of one layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="run paged_kv_write and the decode as two launches instead of the fused "
@@ -303,6 +306,15 @@ def measured_traffic(workload: int, block_size, partition_size: int):
     """HBM bytes per decode call (see recorded_traffic)."""
     return recorded_traffic(TRAFFIC_FILE, DECODE_SOURCE, "decode_source_sha256", workload=workload,
                             block_size=block_size or 16, partition_size=partition_size)
+
+
+MALL_BYTES = 256 << 20  # MI355X Infinity Cache (memory-side, in front of HBM)
+
+
+def cold_replicas(pool_bytes: int) -> int:
+    """Copies of the KV pool to rotate over so that between two uses of one copy
+    the other copies stream at least four times the Infinity Cache through it."""
+    return 1 + max(1, -(-4 * MALL_BYTES // max(pool_bytes, 1)))
 
 
 def to_dev(a, torch):
@@ -592,7 +604,7 @@ def main():
           f"ctx sum={int(wl.steps[0]['ctx'].sum())} setup {time.perf_counter() - t_setup:.1f}s",
           file=sys.stderr, flush=True)
 
-    R = max(1, args.replicas)
+    R = args.replicas if args.replicas > 0 else cold_replicas(wl.w.k_cache.nbytes + wl.w.v_cache.nbytes)
     kcs = [to_dev(wl.w.k_cache, torch) for _ in range(R)]
     vcs = [to_dev(wl.w.v_cache, torch) for _ in range(R)]
     dsteps = []

@@ -702,20 +702,26 @@ __global__ __launch_bounds__(kThreads) void decode_balanced_kernel(
       sm_n[i] = n;
       local += (n + kTile - 1) / kTile;
     }
-    sm_scan[threadIdx.x] = local;
-    __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
-      const int v = (int)threadIdx.x >= off ? sm_scan[threadIdx.x - off] : 0;
-      __syncthreads();
-      sm_scan[threadIdx.x] += v;
-      __syncthreads();
+    // Inclusive scan of `local`: within each wave by lane shuffles, then the
+    // wave totals through LDS (one barrier instead of two per scan step).
+    const int ln = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    int x = local;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(x, off, kWave);
+      if (ln >= off) x += y;
     }
-    int run = sm_scan[threadIdx.x] - local;
+    if (ln == kWave - 1) sm_scan[wv] = x;
+    __syncthreads();
+    int run = x - local;
+    for (int v = 0; v < wv; ++v) run += sm_scan[v];
     for (int i = i0; i < i1; ++i) {
       sm_c[i] = run;
       run += (sm_n[i] + kTile - 1) / kTile;
     }
-    if (threadIdx.x == kThreads - 1) sm_c[num_seqs] = sm_scan[kThreads - 1];
+    // the last thread's running sum is the total (its own sequences included)
+    if (threadIdx.x == kThreads - 1) sm_c[num_seqs] = run;
     __syncthreads();
   }
 
@@ -775,13 +781,17 @@ __global__ __launch_bounds__(kThreads) void decode_balanced_kernel(
     x.n = __builtin_amdgcn_readfirstlane(sm_n[x.s]);
   };
   auto pos_of = [&](int64_t u) {
-    int lo = 0, hi = num_seqs - 1;  // last sequence whose first tile is <= u
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if ((int64_t)num_kv_heads * sm_c[mid] <= u) lo = mid; else hi = mid - 1;
+    // The last sequence whose first tile is <= u: the first tiles do not
+    // decrease, so it is one less than the number of sequences starting at or
+    // before u, counted 64 at a time with a ballot.
+    int count = 0;
+    for (int c = 0; c < num_seqs; c += kWave) {
+      const int j = c + lane;
+      const bool at_or_before = j < num_seqs && (int64_t)num_kv_heads * sm_c[j] <= u;
+      count += __builtin_popcountll(__builtin_amdgcn_ballot_w64(at_or_before));
     }
     Pos x;
-    x.s = __builtin_amdgcn_readfirstlane(lo);
+    x.s = __builtin_amdgcn_readfirstlane(count - 1);
     seq_info(x);
     const int64_t r = u - (int64_t)num_kv_heads * __builtin_amdgcn_readfirstlane(sm_c[x.s]);
     x.g = (int)(r / x.nt);
