@@ -45,6 +45,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "pkv_internal.h"
 
 namespace {
@@ -113,6 +115,18 @@ __device__ inline float group_sum(float x) {
   if constexpr (N >= 16) x += dpp<0x140>(x); // row_mirror
   if constexpr (N >= 32) x += xor16(x);
   if constexpr (N >= 64) x += xor32(x);
+  return x;
+}
+
+// Maximum over aligned groups of N lanes; every lane of a group gets it.
+template <int N>
+__device__ inline float group_max(float x) {
+  if constexpr (N >= 2) x = fmaxf(x, dpp<0xb1>(x));
+  if constexpr (N >= 4) x = fmaxf(x, dpp<0x4e>(x));
+  if constexpr (N >= 8) x = fmaxf(x, dpp<0x141>(x));
+  if constexpr (N >= 16) x = fmaxf(x, dpp<0x140>(x));
+  if constexpr (N >= 32) x = fmaxf(x, xor16(x));
+  if constexpr (N >= 64) x = fmaxf(x, xor32(x));
   return x;
 }
 
@@ -938,17 +952,21 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(
 // One wave per (pair, query head) of the balanced split: pairs covered by
 // several workers are combined here, in worker order,
 // out = sum_w o_w 2^(m_w - m*) / sum_w L_w 2^(m_w - m*).  Pairs finished by a
-// single worker, and pairs of empty sequences, are left alone.  Every lane
-// fetches up to kChunk workers' (m, L) and its D / 64 output dims with
-// independent loads and folds them into a running (max, sum, output).
-// Four such waves share a workgroup: dispatching one-wave workgroups costs
-// about as much as the whole combine.
+// single worker, and pairs of empty sequences, are left alone.  Contributors
+// are taken 64 at a time: lane j fetches contributor j's (m, L), the group's
+// maximum and weighted sum come from wave reductions, and each lane then
+// folds its D / 64 output dims of up to kChunk contributors, fetched with
+// independent loads (8 at a time for pairs of at most 8 workers), so a pair
+// split over up to kChunk workers costs one round trip after the record of
+// its workers.  Four such waves share a
+// workgroup: dispatching one-wave workgroups costs about as much as the whole
+// combine.
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void decode_balanced_reduce_kernel(
     uint16_t* __restrict__ out, const int2* __restrict__ meta, const float* __restrict__ part_ml,
     const float* __restrict__ part_o, int32_t num_pairs, int32_t num_workers) {
   constexpr int DPL = D / kWave;  // dims per lane
-  constexpr int kChunk = 16;
+  constexpr int kChunk = 32;
   static_assert(DPL * kWave == D, "head_dim must be a multiple of 64");
   const int unit = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   if (unit >= num_pairs * G) return;
@@ -964,33 +982,44 @@ __global__ __launch_bounds__(kThreads) void decode_balanced_reduce_kernel(
   float M = -INFINITY, L = 0.0f, O[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) O[e] = 0.0f;
-  for (int k0 = 0; k0 < nseg; k0 += kChunk) {
-    float2 mlv[kChunk];
-    float ov[kChunk][DPL];
-#pragma unroll
-    for (int c = 0; c < kChunk; ++c) {
-      const int64_t k = min(k0 + c, nseg - 1);
-      mlv[c] = *reinterpret_cast<const float2*>(ml + k * 2 * G);
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) ov[c][e] = po[k * G * D + e];
-    }
-    float cm = M;
-#pragma unroll
-    for (int c = 0; c < kChunk; ++c)
-      if (k0 + c < nseg) cm = fmaxf(cm, mlv[c].x);
-    const float a = M == -INFINITY ? 0.0f : exp2f(M - cm);
-    L *= a;
+  for (int k0 = 0; k0 < nseg; k0 += kWave) {
+    const int ng = min(kWave, nseg - k0);  // contributors in this group
+    const bool mine = lane < ng;
+    const float2 v = mine ? *reinterpret_cast<const float2*>(ml + (int64_t)(k0 + lane) * 2 * G)
+                          : make_float2(-INFINITY, 0.0f);
+    const float cm = fmaxf(M, group_max<kWave>(v.x));
+    const float a = M == -INFINITY ? 0.0f : exp2f(M - cm);  // rescales what came before
+    const float f = mine ? exp2f(v.x - cm) : 0.0f;          // lane j: contributor k0 + j's factor
+    L = fmaf(L, a, group_sum<kWave>(v.y * f));
 #pragma unroll
     for (int e = 0; e < DPL; ++e) O[e] *= a;
+    // Output dims of kc contributors at a time (kc = 8 when the group is that
+    // small, else 32): the loads of a chunk are independent, and a small
+    // group does not pay for 32 loads.
+    auto fold = [&](auto kc_tag) {
+      constexpr int kc = decltype(kc_tag)::value;
+      for (int c0 = 0; c0 < ng; c0 += kc) {
+        float ov[kc][DPL];
 #pragma unroll
-    for (int c = 0; c < kChunk; ++c) {
-      if (k0 + c < nseg) {
-        const float f = exp2f(mlv[c].x - cm);
-        L = fmaf(mlv[c].y, f, L);
+        for (int c = 0; c < kc; ++c) {
+          const int64_t k = k0 + min(c0 + c, ng - 1);
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) O[e] = fmaf(ov[c][e], f, O[e]);
+          for (int e = 0; e < DPL; ++e) ov[c][e] = po[k * G * D + e];
+        }
+#pragma unroll
+        for (int c = 0; c < kc; ++c) {
+          if (c0 + c < ng) {
+            const float fc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), c0 + c));
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) O[e] = fmaf(ov[c][e], fc, O[e]);
+          }
+        }
       }
-    }
+    };
+    if (ng <= 8)
+      fold(std::integral_constant<int, 8>{});
+    else
+      fold(std::integral_constant<int, kChunk>{});
     M = cm;
   }
   uint16_t* orow = out + ((int64_t)pair * G + h) * D + lane * DPL;
