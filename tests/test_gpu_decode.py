@@ -243,6 +243,29 @@ def test_balanced_split_edge_cases(case):
     assert np.all(out[ctx == 0] == 0)
 
 
+@pytest.mark.parametrize("tiles,hkv", [(9, 1), (20, 1), (100, 1), (70, 2)])
+def test_balanced_combine_group_sizes(tiles, hkv):
+    """One sequence of `tiles` 16-token tiles per KV head, fewer tiles than
+    workers: every tile is its own worker's share, so each pair is combined
+    from `tiles` partials (just above the 8-contributor round, a clamped
+    32-contributor round, and a second group of contributors past 64)."""
+    print(f"tiles {tiles} hkv {hkv}", flush=True)
+    assert tiles * hkv <= _num_workers()
+    rng = np.random.default_rng(1000 + tiles)
+    S, G, D, B = 1, 4, 128, 16
+    ctx = np.array([tiles * kTILE], np.int32)
+    nb = tiles + 3
+    order = rng.permutation(nb).astype(np.int32)
+    q = normal(rng, (S, hkv * G, D), "bf16")
+    kc = normal(rng, (nb, hkv, B, D), "bf16")
+    vc = normal(rng, (nb, hkv, B, D), "bf16")
+    tables, ctx = _tables(ctx, nb, B, order)
+    poison_unused(kc, vc, tables, ctx, B, "bf16")
+    out = _run_gpu(q, kc, vc, tables, ctx, 1.0 / math.sqrt(D), AUTO)
+    ref = paged_attention_decode(q, kc, vc, tables, ctx, 1.0 / math.sqrt(D), "bf16")
+    print("max_abs/max_rel", check_close(out, ref, "bf16"))
+
+
 def test_balanced_workspace_reused_across_calls():
     """One workspace serves consecutive calls with different context lengths:
     whatever an earlier call left in it never reaches a later result."""
