@@ -423,7 +423,9 @@ def run_prefill(args, torch, pkv):
     T = S * chunk
     nk = datagen.normal(rng, (T, sh.num_kv_heads, sh.head_dim), sh.dtype)
     nv = datagen.normal(rng, (T, sh.num_kv_heads, sh.head_dim), sh.dtype)
-    kc, vc = to_dev(w.k_cache, torch), to_dev(w.v_cache, torch)
+    R = args.replicas if args.replicas > 0 else cold_replicas(w.k_cache.nbytes + w.v_cache.nbytes)
+    kcs = [to_dev(w.k_cache, torch) for _ in range(R)]
+    vcs = [to_dev(w.v_cache, torch) for _ in range(R)]
     d = dict(q=to_dev(w.q, torch), k=to_dev(nk, torch), v=to_dev(nv, torch),
              slots=to_dev(np.concatenate(slots), torch), tables=to_dev(tables, torch),
              ctx=to_dev(ctx, torch), qsl=to_dev(w.qsl, torch))
@@ -431,29 +433,29 @@ def run_prefill(args, torch, pkv):
     stream = torch.cuda.current_stream()
     max_ctx = int(ctx.max())
 
-    def attn():
-        pkv.paged_attention_prefill(out, d["q"], kc, vc, d["tables"], d["ctx"], d["qsl"], sh.scale,
-                                    chunk, max_ctx, stream=stream)
+    def attn(i):
+        pkv.paged_attention_prefill(out, d["q"], kcs[i % R], vcs[i % R], d["tables"], d["ctx"],
+                                    d["qsl"], sh.scale, chunk, max_ctx, stream=stream)
 
-    def step():
-        pkv.paged_kv_write(d["k"], d["v"], d["slots"], kc, vc, stream=stream)
-        attn()
+    def step(i):
+        pkv.paged_kv_write(d["k"], d["v"], d["slots"], kcs[i % R], vcs[i % R], stream=stream)
+        attn(i)
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
-        step()
+    for i in range(args.warmup, args.warmup + args.steps):
+        step(i)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ev2, ev3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev2.record(stream)
-    for _ in range(args.steps):
-        attn()
+    for i in range(args.warmup, args.warmup + args.steps):
+        attn(i)
     ev3.record(stream)
     torch.cuda.synchronize()
     attn_ms = ev2.elapsed_time(ev3) / args.steps
@@ -470,7 +472,7 @@ def run_prefill(args, torch, pkv):
         "config": {"workload": WORKLOAD_NAMES[7], "num_seqs": S, "new_tokens": T,
                    "num_q_heads": sh.num_q_heads, "num_kv_heads": sh.num_kv_heads,
                    "head_dim": sh.head_dim, "block_size": B, "pool_blocks": w.num_blocks,
-                   "mean_context": float(ctx.mean())},
+                   "mean_context": float(ctx.mean()), "replicas": R},
         "attn_ms": round(attn_ms, 4),
         "tokens_per_s": round(T / (attn_ms * 1e-3), 1),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
