@@ -62,6 +62,10 @@ constexpr int kKeys = 32;                             // keys per K/V tile
 // A tile's row maximum must exceed the reference maximum by more than this
 // (log2 units) before that row's accumulators are rescaled; weights <= 2^8.
 constexpr float kRescaleSlack = 8.0f;
+// A weight of at least this shows that its row's maximum may exceed the
+// reference by more than kRescaleSlack (2^8 = 256, less a margin for exp2's
+// rounding).
+constexpr float kGrowWeight = 255.5f;
 
 // D = A B + C on a 16x16x32 bf16 tile.  Lane l supplies row (l % 16) of A and
 // column (l % 16) of B, each as 8 consecutive k-slots of group l / 16; it
@@ -458,7 +462,6 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(
     for (int c = 0; c < 2; ++c) {
       // raw logits; qscale > 0, so the scaled maximum is qscale * max
       float x[2][4];
-      float mx = -INFINITY;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -466,24 +469,50 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(
           const int t = tbase + 16 * h + r;
           x[h][r] = sc[c][h][r];
           if constexpr (kMasked) x[h][r] = t <= pos[c] ? x[h][r] : -INFINITY;
-          mx = fmaxf(mx, x[h][r]);
         }
-      mx = rows_max(mx) * qscale;
-      const bool grow = mx > m[c] + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float alpha = grow ? fast_exp2(m[c] - mx) : 1.0f;
-        if (grow) m[c] = mx;
-        lsum[c] *= alpha;
+      // Weights against the running reference.  The row maximum only matters
+      // when it exceeds the reference by more than the slack, and then some
+      // weight is at least 2^slack; below a threshold just under that no row
+      // can grow, so the maximum is computed only when a weight reaches it
+      // (always on the first tile, whose reference is -inf).  The rescale
+      // then follows the same test as always, and the weights are recomputed
+      // against the new reference: the result is the same bit for bit.
+      float p[2][4];
+      float pmax = 0.0f;
 #pragma unroll
-        for (int t = 0; t < DT; ++t) o[c][t] *= alpha;
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[h][r] = fast_exp2(fmaf(x[h][r], qscale, -m[c]));
+          pmax = fmaxf(pmax, p[h][r]);
+        }
+      if (__builtin_amdgcn_ballot_w64(!(pmax < kGrowWeight))) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, x[h][r]);
+        mx = rows_max(mx) * qscale;
+        const bool grow = mx > m[c] + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          const float alpha = grow ? fast_exp2(m[c] - mx) : 1.0f;
+          if (grow) m[c] = mx;
+          lsum[c] *= alpha;
+#pragma unroll
+          for (int t = 0; t < DT; ++t) o[c][t] *= alpha;
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[h][r] = fast_exp2(fmaf(x[h][r], qscale, -m[c]));
+        }
       }
       uint32_t ph[4], plo[4];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int r = 0; r < 4; r += 2) {
-          const float p0 = fast_exp2(fmaf(x[h][r], qscale, -m[c]));
-          const float p1 = fast_exp2(fmaf(x[h][r + 1], qscale, -m[c]));
+          const float p0 = p[h][r];
+          const float p1 = p[h][r + 1];
           lsum[c] += p0 + p1;
           const uint32_t hp = pack_bf16(p0, p1);
           ph[2 * h + r / 2] = hp;
