@@ -114,6 +114,17 @@ size_t pkv_decode_workspace_bytes(const pkv_cache_desc* c, int32_t num_seqs,
                                   int32_t partition_size);
 
 /*
+ * The most sequences one balanced-split decode takes on the current HIP
+ * device (-1 with pkv_last_error() set if the device cannot be queried).
+ * Every workgroup of that split keeps each sequence's context length and
+ * tile prefix sum in LDS, 8 bytes per sequence, within the share of a
+ * compute unit's LDS that one of its workgroups may use (two workgroups per
+ * compute unit): 10237 sequences on MI355X's 160 KiB.  Larger batches run in
+ * split-context partitions of 512 tokens.
+ */
+int32_t pkv_decode_balanced_max_seqs(void);
+
+/*
  * Decode attention: one query token per sequence against that sequence's
  * cached K/V, read through its block table (blog section 3(3), step 2:
  * attention is computed over the logically contiguous tokens while the data
@@ -140,8 +151,8 @@ size_t pkv_decode_workspace_bytes(const pkv_cache_desc* c, int32_t num_seqs,
  *                 counts the token just written by pkv_paged_kv_write
  *   max_context_len  host int, bound on context_lens (sizes the launch)
  *   partition_size   how the work is split:
- *                 PKV_PARTITION_AUTO: bf16 caches with num_seqs <= 8191 use a
- *                   balanced split: every worker wave of the GPU reads an
+ *                 PKV_PARTITION_AUTO: bf16 caches with num_seqs <=
+ *                   pkv_decode_balanced_max_seqs() use a balanced split: every worker wave of the GPU reads an
  *                   equal share of all sequences' 16-token tiles (ragged
  *                   context lengths cannot unbalance it), and the sequences
  *                   whose tiles several workers share are combined by a second
@@ -180,7 +191,8 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
  * The slot of position n - 1 must not be shared with another sequence (the
  * allocator's copy-on-write guarantees this; run pkv_copy_blocks first).
  * Sequences with n = 0 append nothing.  Runs the balanced split only: bf16
- * caches and num_seqs <= 8191 (PKV_EUNSUPPORTED otherwise).  Workspace as for
+ * caches and num_seqs <= pkv_decode_balanced_max_seqs() (PKV_EUNSUPPORTED
+ * otherwise).  Workspace as for
  * pkv_decode_workspace_bytes(..., PKV_PARTITION_AUTO).
  * Errors: as pkv_paged_attention_decode.
  */

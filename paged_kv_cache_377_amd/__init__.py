@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     PagedKVError,
     cache_desc,
     copy_blocks,
+    decode_balanced_max_seqs,
     decode_workspace_bytes,
     header_functions,
     lib,

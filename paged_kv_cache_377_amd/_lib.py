@@ -60,6 +60,7 @@ _SIGS = {
     "pkv_paged_kv_write": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _P(CacheDesc), _vp]),
     "pkv_copy_blocks": (_i32, [_vp, _vp, _P(CacheDesc), _vp, _i32, _vp]),
     "pkv_decode_workspace_bytes": (_sz, [_P(CacheDesc), _i32, _i32, _i32, _i32]),
+    "pkv_decode_balanced_max_seqs": (_i32, []),
     "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _P(CacheDesc), _vp, _i32, _vp, _i32,
                                           _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pkv_paged_attention_decode_append": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _P(CacheDesc), _vp,
@@ -176,12 +177,37 @@ def cache_desc(k_cache) -> CacheDesc:
     return CacheDesc(nb, hkv, bs, d, _dtype_code(k_cache))
 
 
+def _check_pools(k_pool, v_pool, what: str = "k_cache and v_cache") -> None:
+    """The library sizes both pools from one descriptor built from the K pool:
+    a V pool of another shape or dtype would be read or written out of bounds."""
+    if k_pool.dim() != 4:
+        raise PagedKVError(PKV_EINVAL, f"{what}: pools must be [num_blocks, Hkv, B, D]")
+    if v_pool.shape != k_pool.shape or v_pool.dtype != k_pool.dtype:
+        raise PagedKVError(PKV_EINVAL, f"{what} differ: {tuple(k_pool.shape)} {k_pool.dtype} "
+                                       f"against {tuple(v_pool.shape)} {v_pool.dtype}")
+
+
+def _check_rows(q, out, k_cache) -> None:
+    """q and out are [rows, Hq, D] of the cache's dtype and head_dim, Hq a
+    multiple of the cache's KV heads (the kernels index them with the cache's
+    head_dim)."""
+    if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype or q.dtype != k_cache.dtype:
+        raise PagedKVError(PKV_EINVAL, "out/q/cache dtype or shape mismatch")
+    if q.shape[2] != k_cache.shape[3]:
+        raise PagedKVError(PKV_EINVAL, f"q head_dim {q.shape[2]} != cache head_dim "
+                                       f"{k_cache.shape[3]}")
+    if q.shape[1] % k_cache.shape[1] != 0:
+        raise PagedKVError(PKV_EINVAL, f"query heads {q.shape[1]} not a multiple of KV heads "
+                                       f"{k_cache.shape[1]}")
+
+
 def paged_kv_write(k, v, slot_mapping, k_cache, v_cache, stream=None) -> None:
     """k, v: [T, Hkv, D]; slot_mapping: [T] int64; caches [NB, Hkv, B, D] (device)."""
     torch = _torch()
     if slot_mapping.dtype != torch.int64:
         raise PagedKVError(PKV_EINVAL, "slot_mapping must be int64")
-    if k.dtype != k_cache.dtype or v.dtype != v_cache.dtype or k_cache.shape != v_cache.shape:
+    _check_pools(k_cache, v_cache)
+    if k.dtype != k_cache.dtype or v.dtype != v_cache.dtype:
         raise PagedKVError(PKV_EINVAL, "k/v and caches must share dtype and shape")
     T = slot_mapping.numel()
     if k.shape != (T, k_cache.shape[1], k_cache.shape[3]) or v.shape != k.shape:
@@ -196,8 +222,7 @@ def copy_blocks(k_cache, v_cache, src_dst_pairs, stream=None) -> None:
     torch = _torch()
     if src_dst_pairs.dtype != torch.int32 or (src_dst_pairs.numel() and src_dst_pairs.shape[-1] != 2):
         raise PagedKVError(PKV_EINVAL, "src_dst_pairs must be int32 [n, 2]")
-    if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype:
-        raise PagedKVError(PKV_EINVAL, "k_cache and v_cache must match")
+    _check_pools(k_cache, v_cache)
     desc = cache_desc(k_cache)
     n = src_dst_pairs.numel() // 2
     _check(lib().pkv_copy_blocks(_ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
@@ -216,6 +241,14 @@ def decode_workspace_bytes(desc: CacheDesc, num_seqs: int, num_q_heads: int,
     return n
 
 
+def decode_balanced_max_seqs() -> int:
+    """The most sequences a balanced-split decode takes on the current device."""
+    n = int(lib().pkv_decode_balanced_max_seqs())
+    if n < 0:
+        raise PagedKVError(PKV_EHIP, lib().pkv_last_error().decode())
+    return n
+
+
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
                            max_context_len: int, partition_size: int = PKV_PARTITION_AUTO,
                            workspace=None, stream=None) -> None:
@@ -228,9 +261,9 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     bytes; if None, one is allocated with torch (plumbing, outside the kernels).
     """
     torch = _torch()
+    _check_pools(k_cache, v_cache)
+    _check_rows(q, out, k_cache)
     S, Hq, D = q.shape
-    if out.shape != q.shape or out.dtype != q.dtype or q.dtype != k_cache.dtype:
-        raise PagedKVError(PKV_EINVAL, "out/q/cache dtype or shape mismatch")
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise PagedKVError(PKV_EINVAL, "block_tables and context_lens must be int32")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
@@ -254,9 +287,9 @@ def paged_attention_decode_append(out, q, k_new, v_new, k_cache, v_cache, block_
     """Write k_new / v_new [S, Hkv, D] at each sequence's last position and
     decode, in one launch (the balanced split)."""
     torch = _torch()
+    _check_pools(k_cache, v_cache)
+    _check_rows(q, out, k_cache)
     S, Hq, D = q.shape
-    if out.shape != q.shape or out.dtype != q.dtype or q.dtype != k_cache.dtype:
-        raise PagedKVError(PKV_EINVAL, "out/q/cache dtype or shape mismatch")
     if k_new.shape != (S, k_cache.shape[1], D) or v_new.shape != k_new.shape \
             or k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
         raise PagedKVError(PKV_EINVAL, "k_new and v_new must be [S, Hkv, D] of the cache dtype")
@@ -284,9 +317,9 @@ def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens
     [S + 1] int32.  ``max_new_tokens`` / ``max_context_len`` are host-side
     bounds of the per-sequence new-token counts and context lengths."""
     torch = _torch()
+    _check_pools(k_cache, v_cache)
+    _check_rows(q, out, k_cache)
     T, Hq, D = q.shape
-    if out.shape != q.shape or out.dtype != q.dtype or q.dtype != k_cache.dtype:
-        raise PagedKVError(PKV_EINVAL, "out/q/cache dtype or shape mismatch")
     if (block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32
             or query_start_loc.dtype != torch.int32):
         raise PagedKVError(PKV_EINVAL, "block_tables, context_lens and query_start_loc must be int32")
@@ -307,6 +340,8 @@ def swap_blocks(dst_k, dst_v, src_k, src_v, pairs, stream=None) -> None:
     torch = _torch()
     if pairs.dtype != torch.int32 or (pairs.numel() and (pairs.dim() != 2 or pairs.shape[1] != 2)):
         raise PagedKVError(PKV_EINVAL, "pairs must be [n, 2] int32")
+    _check_pools(dst_k, dst_v, "dst_k and dst_v")
+    _check_pools(src_k, src_v, "src_k and src_v")
     if dst_k.shape[1:] != src_k.shape[1:] or dst_k.dtype != src_k.dtype:
         raise PagedKVError(PKV_EINVAL, "pools differ in block shape or dtype")
     desc = cache_desc(dst_k)

@@ -45,6 +45,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "pkv_internal.h"
@@ -612,10 +614,13 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_kernel(
   const int32_t* bt = block_tables + (int64_t)s * table_width;
   const uint16_t* safe = q + 8 * grp;
 
-  auto load_tile = [&](int tile, int cb0, KVTile<D>& x) {
+  // A live row of the chunk [c0, c1) lies at or before the chunk's last
+  // position `last`; a dead row (tile -1 or past t1) reads the table entry of
+  // `last`, so the LDS index stays below the chunk's staged entry count.
+  auto load_tile = [&](int tile, int cb0, int last, KVTile<D>& x) {
     const int t = t0 + tile * kTile + col;
     const bool live = tile >= 0 && t < t1;
-    const int tc = live ? t : t1 - 1;  // stays inside the staged chunk
+    const int tc = live ? t : last;
     load_kv<D, B>(x, k_cache, v_cache, safe, live, sm_bt[tc / B - cb0], tc, g, num_kv_heads,
                   num_blocks, grp);
   };
@@ -637,14 +642,15 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_kernel(
     // is padded to an even number so the loop has a single exit, which keeps
     // the compiler's load counting exact across the back edge.
     const int mine = (c1 - 1 - tile) / kWaves + 1;
+    const int last = min(t1, t0 + c1 * kTile) - 1;  // the chunk's last position
     KVTile<D> ta, tb;
-    load_tile(tile, cb0, ta);
+    load_tile(tile, cb0, last, ta);
     for (int it = 0; it < (mine + 1) / 2; ++it, tile += 2 * kWaves) {
       const int t_b = tile + kWaves;
       const int t_c = tile + 2 * kWaves;
-      load_tile(t_b < c1 ? t_b : -1, cb0, tb);
+      load_tile(t_b < c1 ? t_b : -1, cb0, last, tb);
       at.update(ta, min(kTile, t1 - (t0 + tile * kTile)), qscale, grp);
-      load_tile(t_c < c1 ? t_c : -1, cb0, ta);
+      load_tile(t_c < c1 ? t_c : -1, cb0, last, ta);
       if (t_b < c1) at.update(tb, min(kTile, t1 - (t0 + t_b * kTile)), qscale, grp);
     }
   }
@@ -701,7 +707,7 @@ __global__ __launch_bounds__(kThreads) void decode_balanced_kernel(
   extern __shared__ int32_t sm_dyn[];
   int32_t* sm_c = sm_dyn;                 // [num_seqs + 1] tiles of one KV head before sequence s
   int32_t* sm_n = sm_dyn + num_seqs + 1;  // [num_seqs] clamped context lengths
-  __shared__ int32_t sm_scan[kThreads];
+  __shared__ int32_t sm_scan[kWaves];  // wave totals of the scan
 
   // Prefix sums of the tile counts (every workgroup computes its own copy).
   {
@@ -1029,8 +1035,10 @@ __global__ __launch_bounds__(kThreads) void decode_balanced_reduce_kernel(
 
 // ------------------------------------------------------------- dispatch
 
-constexpr int kMaxSeqsBalanced = 8191;  // prefix sums and lengths fit 64 KiB of LDS
 constexpr int kWorkerWavesPerSimd = 2;  // the balanced kernel's occupancy (VGPR-bound)
+// Static LDS of the balanced kernel (the wave totals of its scan, sm_scan);
+// the dynamic part is (2 num_seqs + 1) int32 of prefix sums and lengths.
+constexpr int kBalancedStaticLds = kWaves * (int)sizeof(int32_t);
 
 // How one call is split and where its workspace pieces go.
 struct Plan {
@@ -1043,22 +1051,43 @@ struct Plan {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workers of the balanced split: the waves the current device holds at once.
-int workers_for_device(int32_t* nw) {
-  static int cache[64];
+// What the balanced split needs to know about the current device: its
+// workers (the waves it holds at once: CUs x 4 SIMDs x kWorkerWavesPerSimd)
+// and the most sequences whose prefix sums and lengths fit the LDS one of its
+// workgroups may use.  The grid puts kWorkerWavesPerSimd workgroups on every
+// CU, so a workgroup may use a 1 / kWorkerWavesPerSimd share of the CU's LDS
+// (and no more than the per-workgroup maximum).
+struct DeviceLimits {
+  int32_t workers;
+  int32_t max_seqs;
+};
+
+int device_limits(DeviceLimits* out) {
+  static std::mutex mu;
+  static DeviceLimits cache[64];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return pkv__fail(PKV_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
-    *nw = cache[dev];
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev >= 0 && dev < 64 && cache[dev].workers > 0) {
+    *out = cache[dev];
     return PKV_OK;
   }
-  int cus = 0;
+  int cus = 0, lds_cu = 0, lds_block = 0;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess || cus <= 0)
-    return pkv__fail(PKV_EHIP, "compute unit count: %s", hipGetErrorString(e));
-  *nw = cus * 4 * kWorkerWavesPerSimd;
-  if (dev >= 0 && dev < 64) cache[dev] = *nw;
+  if (e == hipSuccess)
+    e = hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+  if (e == hipSuccess)
+    e = hipDeviceGetAttribute(&lds_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+  if (e != hipSuccess || cus <= 0 || lds_cu <= 0 || lds_block <= 0)
+    return pkv__fail(PKV_EHIP, "device attributes: %s", hipGetErrorString(e));
+  const int budget = std::min(lds_block, lds_cu / kWorkerWavesPerSimd);
+  DeviceLimits d;
+  d.workers = cus * 4 * kWorkerWavesPerSimd;
+  d.max_seqs = std::max(0, (budget - kBalancedStaticLds - (int)sizeof(int32_t)) /
+                               (2 * (int)sizeof(int32_t)));
+  if (dev >= 0 && dev < 64) cache[dev] = d;
+  *out = d;
   return PKV_OK;
 }
 
@@ -1069,10 +1098,13 @@ int make_plan(const pkv_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
   *pl = Plan{};
   if (partition_size == PKV_PARTITION_AUTO) {
     const int64_t tiles_per_head = (int64_t)num_seqs * ((max_context_len + kTile - 1) / kTile);
-    if (c->dtype == PKV_BF16 && num_seqs <= kMaxSeqsBalanced && tiles_per_head < (1 << 30)) {
-      int32_t nw = 0;
-      int rc = workers_for_device(&nw);
+    DeviceLimits lim{0, 0};
+    if (c->dtype == PKV_BF16) {
+      int rc = device_limits(&lim);
       if (rc) return rc;
+    }
+    if (c->dtype == PKV_BF16 && num_seqs <= lim.max_seqs && tiles_per_head < (1 << 30)) {
+      const int32_t nw = lim.workers;
       const size_t pairs = (size_t)num_seqs * c->num_kv_heads;
       const size_t slots = (pairs + (size_t)nw) * G;
       pl->balanced = true;
@@ -1253,6 +1285,13 @@ extern "C" size_t pkv_decode_workspace_bytes(const pkv_cache_desc* c, int32_t nu
   return pl.bytes;
 }
 
+extern "C" int32_t pkv_decode_balanced_max_seqs(void) {
+  pkv__clear_error();
+  DeviceLimits lim;
+  if (device_limits(&lim)) return -1;
+  return lim.max_seqs;
+}
+
 namespace {
 
 int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
@@ -1282,7 +1321,7 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
     if (!pl.balanced)
       return pkv__fail(PKV_EUNSUPPORTED,
                        "the fused append runs in the balanced split only (bf16 caches, "
-                       "PKV_PARTITION_AUTO, num_seqs <= %d)", kMaxSeqsBalanced);
+                       "PKV_PARTITION_AUTO, num_seqs <= pkv_decode_balanced_max_seqs())");
     if (!aligned16(k_new) || !aligned16(v_new))
       return pkv__fail(PKV_EINVAL, "k_new and v_new must be 16-byte aligned");
   }

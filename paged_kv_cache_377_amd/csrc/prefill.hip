@@ -387,7 +387,9 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(
     const int j = j0 + r / G;
     row_tok[c] = q0 + j;
     row_head[c] = g * G + r % G;
-    row_ok[c] = j < jend && q0 + j < num_tokens;
+    // query_start_loc entries outside [0, num_tokens] break the contract;
+    // such rows are neither read nor written
+    row_ok[c] = j < jend && q0 + j >= 0 && q0 + j < num_tokens;
     // rows past the tile's tokens act as its last token (their output is
     // dropped), so no row is masked everywhere
     pos[c] = row_ok[c] ? first + j : pmax;
