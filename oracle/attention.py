@@ -80,10 +80,13 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens,
             continue
         blocks = [int(block_tables[s][t // B]) for t in range(n)]
         offsets = [t % B for t in range(n)]
+        gathered = {}  # KV head -> its gathered (K, V), shared by the head's G query heads
         for h in head_list:
             g = h // G
-            K = to_f64(k_cache[blocks, g, offsets, :], dtype)   # [n, D]
-            V = to_f64(v_cache[blocks, g, offsets, :], dtype)   # [n, D]
+            if g not in gathered:
+                gathered[g] = (to_f64(k_cache[blocks, g, offsets, :], dtype),   # [n, D]
+                               to_f64(v_cache[blocks, g, offsets, :], dtype))   # [n, D]
+            K, V = gathered[g]
             qh = to_f64(q[s, h, :], dtype)                      # [D]
             logits = scale * (K @ qh)                           # [n]
             w = np.exp(logits - logits.max())
@@ -122,10 +125,13 @@ def paged_attention_prefill(q, k_cache, v_cache, block_tables, context_lens, que
         first = n - n_new
         blocks = [int(block_tables[s][t // B]) for t in range(n)]
         offsets = [t % B for t in range(n)]
+        gathered = {}  # KV head -> its gathered (K, V), shared by the head's G query heads
         for h in head_list:
             g = h // G
-            K = to_f64(k_cache[blocks, g, offsets, :], dtype)   # [n, D]
-            V = to_f64(v_cache[blocks, g, offsets, :], dtype)
+            if g not in gathered:
+                gathered[g] = (to_f64(k_cache[blocks, g, offsets, :], dtype),   # [n, D]
+                               to_f64(v_cache[blocks, g, offsets, :], dtype))
+            K, V = gathered[g]
             for j in range(n_new):
                 p = first + j
                 qh = to_f64(q[qsl[s] + j, h, :], dtype)

@@ -87,9 +87,8 @@ def test_full_size_llama_layer():
     torch.cuda.synchronize()
     ek, ev = paged_kv_write(nk, nv, slots, kc, vc)
     assert np.array_equal(host(k2), ek) and np.array_equal(host(v2), ev)
-    sample = sorted({0, len(lens) - 1, int(np.argmax(ctx)), int(np.argmin(ctx))})
-    ref = paged_attention_decode(q, ek, ev, tables, ctx, sh.scale, "bf16", seqs=sample)
-    check_close(host(o2)[sample], ref[sample], "bf16")
+    ref = paged_attention_decode(q, ek, ev, tables, ctx, sh.scale, "bf16")
+    print("fused full size max_abs/max_rel", check_close(host(o2), ref, "bf16"))
 
 
 def test_fp32_caches_are_not_built_for_the_fused_path():

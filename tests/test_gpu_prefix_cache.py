@@ -11,7 +11,7 @@ a token to every request (ids given, so blocks they fill would be entered).
 A position's K/V depend on its whole token prefix, so the system prompt's
 rows are the same for every request and each question's rows are its own.
 Every live slot of the GPU pool must hold, bit for bit, the row the oracle's
-allocator maps there, and the decode of sampled requests must match the
+allocator maps there, and the decode of every request must match the
 oracle's attention over each request's full history.
 """
 
@@ -97,7 +97,5 @@ def test_shared_system_prompt_full_size():
     t_np, l_np = np.array(tables, np.int32), np.array(lens, np.int32)
     pkv.paged_attention_decode(out, dev(q), kc, vc, dev(t_np), dev(l_np), sh.scale, int(l_np.max()))
     torch.cuda.synchronize()
-    sample = sorted({0, 1, R - 1, int(np.argmax(l_np)), int(np.argmin(l_np))} |
-                    set(rng.choice(R, 6, replace=False).tolist()))
-    ref = paged_attention_decode(q, ek, ev, t_np, l_np, sh.scale, sh.dtype, seqs=sample)
-    print("prefix decode max_abs/max_rel", check_close(host(out)[sample], ref[sample], sh.dtype))
+    ref = paged_attention_decode(q, ek, ev, t_np, l_np, sh.scale, sh.dtype)
+    print("prefix decode max_abs/max_rel", check_close(host(out), ref, sh.dtype))

@@ -6,7 +6,7 @@
   pairs, paged_kv_write of the new tokens.  At the end every live slot of the
   GPU pool must hold, bit for bit, the token the oracle's allocator maps there
   (blog section 4: a sample's copy of the shared block carries the prompt's
-  tokens before its own token lands), and the decode of sampled sequences must
+  tokens before its own token lands), and the decode of every sequence must
   match the oracle's.
 * Mixed step: 256 sequences with log-uniform contexts, one step that appends a
   token to every sequence (allocator step + paged_kv_write) and decodes, for
@@ -98,12 +98,11 @@ def test_parallel_sampling_full_size():
     t_np, l_np = np.array(tables, np.int32), np.array(lens, np.int32)
     pkv.paged_attention_decode(out, dq, kc, vc, dev(t_np), dev(l_np), sh.scale, int(l_np.max()))
     torch.cuda.synchronize()
-    sample = sorted(set(range(8)) | set(rng.choice(S, 8, replace=False).tolist()))
-    ref = paged_attention_decode(q, ek, ev, t_np, l_np, sh.scale, sh.dtype, seqs=sample)
-    print("sampling decode max_abs/max_rel", check_close(host(out)[sample], ref[sample], sh.dtype))
+    ref = paged_attention_decode(q, ek, ev, t_np, l_np, sh.scale, sh.dtype)
+    print("sampling decode max_abs/max_rel", check_close(host(out), ref, sh.dtype))
 
 
-@pytest.mark.parametrize("block_size,num_seqs", [(16, None), (8, 64), (32, 64)])
+@pytest.mark.parametrize("block_size,num_seqs", [(16, None), (8, None), (32, None)])
 def test_mixed_step_full_size(block_size, num_seqs):
     """The step of the mixed workload: prefix admitted and written, then one
     appended token per sequence (allocator step + write), then the decode."""
@@ -150,8 +149,5 @@ def test_mixed_step_full_size(block_size, num_seqs):
     assert np.array_equal(gk[blk, :, offs, :], nk) and np.array_equal(gv[blk, :, offs, :], nv)
     assert np.array_equal(live_rows(gk, tables, lens, B), live_rows(ek, tables, lens, B))
     assert np.array_equal(live_rows(gv, tables, lens, B), live_rows(ev, tables, lens, B))
-    rng = np.random.default_rng(5)
-    sample = sorted({int(np.argmax(l_np)), int(np.argmin(l_np)), 0, S - 1} |
-                    set(rng.choice(S, 6, replace=False).tolist()))
-    ref = paged_attention_decode(w.q, ek, ev, t_np, l_np, sh.scale, sh.dtype, seqs=sample)
-    print("mixed decode max_abs/max_rel", check_close(host(out)[sample], ref[sample], sh.dtype))
+    ref = paged_attention_decode(w.q, ek, ev, t_np, l_np, sh.scale, sh.dtype)
+    print("mixed decode max_abs/max_rel", check_close(host(out), ref, sh.dtype))
