@@ -99,6 +99,9 @@ int pkv_paged_kv_write(const void* k, const void* v, const int64_t* slot_mapping
 int pkv_copy_blocks(void* k_cache, void* v_cache, const pkv_cache_desc* c,
                     const int32_t* src_dst_pairs, int32_t num_pairs, void* stream);
 
+/* Size of the per-device array pkv_paged_attention_decode_noalloc works in. */
+#define PKV_DECODE_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+
 /* partition_size value: let the library split the work (see below). */
 enum { PKV_PARTITION_AUTO = -1 };
 
@@ -179,6 +182,29 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
                                int32_t num_q_heads, int32_t max_context_len, float scale,
                                int32_t partition_size, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_paged_attention_decode without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The workspace is a
+ * library-owned device array of PKV_DECODE_NOALLOC_MAX_BYTES bytes
+ * (32 MiB), one per device, held until the process ends; its address is
+ * looked up on the first call made on a device and the call allocates
+ * nothing.  Arguments, results and errors as pkv_paged_attention_decode,
+ * plus PKV_EINVAL when pkv_decode_workspace_bytes(...) for these sizes
+ * exceeds the array (nothing is launched then): 17 MiB is the most any of
+ * the decode workloads here needs (256 sequences, 8 KV heads, G = 8).
+ * Nothing in the array needs to start at zero: every call writes what it
+ * reads.  All calls on one device share its array, so calls on one device
+ * that may overlap (different streams, or host threads without ordering)
+ * race and give unspecified results; calls ordered on one stream do not.
+ */
+int pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_cache,
+                                       const void* v_cache, const pkv_cache_desc* c,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t max_context_len,
+                                       float scale, int32_t partition_size, void* stream);
 
 /*
  * Append + decode in one launch: for each sequence s with n = context_lens[s]

@@ -28,6 +28,8 @@ from ._lib import (  # noqa: F401
     lib,
     paged_attention_decode,
     paged_attention_decode_append,
+    paged_attention_decode_noalloc,
+    decode_noalloc_max_bytes,
     paged_attention_prefill,
     paged_kv_write,
     swap_blocks,

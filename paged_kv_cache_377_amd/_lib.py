@@ -63,6 +63,8 @@ _SIGS = {
     "pkv_decode_balanced_max_seqs": (_i32, []),
     "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _P(CacheDesc), _vp, _i32, _vp, _i32,
                                           _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
+    "pkv_paged_attention_decode_noalloc": (_i32, [_vp, _vp, _vp, _vp, _P(CacheDesc), _vp, _i32, _vp,
+                                                  _i32, _i32, _i32, _f32, _i32, _vp]),
     "pkv_paged_attention_decode_append": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _P(CacheDesc), _vp,
                                                  _i32, _vp, _i32, _i32, _i32, _f32, _vp, _sz,
                                                  _vp]),
@@ -279,6 +281,33 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S, Hq,
         int(max_context_len), float(scale), int(partition_size), _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+def paged_attention_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens,
+                                   scale: float, max_context_len: int,
+                                   partition_size: int = PKV_PARTITION_AUTO, stream=None) -> None:
+    """paged_attention_decode with the library's per-device scratch array as
+    workspace: nothing is allocated (calls on one device must not overlap)."""
+    torch = _torch()
+    _check_pools(k_cache, v_cache)
+    _check_rows(q, out, k_cache)
+    S, Hq, D = q.shape
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise PagedKVError(PKV_EINVAL, "block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise PagedKVError(PKV_EINVAL, "block_tables must be [S, M] and context_lens [S]")
+    desc = cache_desc(k_cache)
+    _check(lib().pkv_paged_attention_decode_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S, Hq,
+        int(max_context_len), float(scale), int(partition_size), _stream(stream)))
+
+
+def decode_noalloc_max_bytes() -> int:
+    """PKV_DECODE_NOALLOC_MAX_BYTES of include/pagedkv.h."""
+    text = open(HEADER).read()
+    m = re.search(r"#define PKV_DECODE_NOALLOC_MAX_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    return int(m.group(1)) << int(m.group(2))
 
 
 def paged_attention_decode_append(out, q, k_new, v_new, k_cache, v_cache, block_tables,

@@ -1374,6 +1374,73 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
                      scale, partition_size, workspace, workspace_bytes, stream);
 }
 
+// ------------------------------------------------- allocation-free variant
+//
+// pkv_paged_attention_decode_noalloc keeps its workspace (the balanced split's
+// worker records and partials, or the split-context partials) in this
+// file-scope device array instead of a caller-supplied buffer.  Every device
+// the library runs on holds its own copy until the process ends.  On the host
+// `scratch` only names the symbol: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+constexpr size_t kScratchBytes = PKV_DECODE_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device (looked up on the first
+// call made with that device current).
+int scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return pkv__fail(PKV_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return pkv__fail(PKV_EUNSUPPORTED, "device %d: the scratch table holds %d devices", dev,
+                     kMaxDevices);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return pkv__fail(PKV_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" int pkv_paged_attention_decode_noalloc(
+    void* out, const void* q, const void* k_cache, const void* v_cache, const pkv_cache_desc* c,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len, float scale,
+    int32_t partition_size, void* stream) {
+  pkv__clear_error();
+  int rc = check_sizes(c, num_seqs, num_q_heads, max_context_len, partition_size);
+  if (rc) return rc;
+  if (num_seqs == 0) return PKV_OK;
+  Plan pl;
+  rc = make_plan(c, num_seqs, num_q_heads, max_context_len, partition_size, &pl);
+  if (rc) return rc;
+  if (pl.bytes > kScratchBytes)
+    return pkv__fail(PKV_EINVAL,
+                     "this decode needs %zu bytes of workspace, more than the %zu bytes of "
+                     "library scratch; call pkv_paged_attention_decode with a workspace",
+                     pl.bytes, kScratchBytes);
+  void* ws = nullptr;
+  if (pl.bytes) {
+    rc = scratch_address(&ws);
+    if (rc) return rc;
+  }
+  return decode_impl(out, q, nullptr, nullptr, k_cache, v_cache, c, block_tables,
+                     max_blocks_per_seq, context_lens, num_seqs, num_q_heads, max_context_len,
+                     scale, partition_size, ws, ws ? kScratchBytes : 0, stream);
+}
+
 extern "C" int pkv_paged_attention_decode_append(
     void* out, const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
     const pkv_cache_desc* c, const int32_t* block_tables, int32_t max_blocks_per_seq,

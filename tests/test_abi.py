@@ -10,6 +10,7 @@ import paged_kv_cache_377_amd as pkv
 def test_every_declared_symbol_is_exported():
     names = pkv.header_functions()
     assert len(names) >= 19
+    assert "pkv_paged_attention_decode_noalloc" in names
     lib = pkv.lib()
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
