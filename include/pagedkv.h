@@ -120,10 +120,10 @@ size_t pkv_decode_workspace_bytes(const pkv_cache_desc* c, int32_t num_seqs,
  * The most sequences one balanced-split decode takes on the current HIP
  * device (-1 with pkv_last_error() set if the device cannot be queried).
  * Every workgroup of that split keeps each sequence's context length and
- * tile prefix sum in LDS, 8 bytes per sequence, within the share of a
- * compute unit's LDS that one of its workgroups may use (two workgroups per
- * compute unit): 10237 sequences on MI355X's 160 KiB.  Larger batches run in
- * split-context partitions of 512 tokens.
+ * tile prefix sum in LDS, 8 bytes per sequence, within the LDS one of its
+ * workgroups may use (one workgroup per compute unit): 20475 sequences on
+ * MI355X's 160 KiB.  Larger batches run in split-context partitions of 512
+ * tokens.
  */
 int32_t pkv_decode_balanced_max_seqs(void);
 

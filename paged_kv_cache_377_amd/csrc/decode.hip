@@ -674,44 +674,55 @@ __global__ __launch_bounds__(kThreads) void decode_partition_mfma_kernel(
 
 // ------------------------------------------------------ balanced (bf16)
 //
-// The work is the list of all 16-token tiles of all (sequence, KV head) pairs,
-// numbered pair by pair (sequence, then KV head, then tile).  Each wave is a
-// worker that takes one contiguous, equal share [w T / nw, (w + 1) T / nw) of
-// the T tiles, so every worker reads the same number of K/V bytes however
-// ragged the context lengths are, and streams its share with the next tiles'
-// loads always in flight.  nw = min(T, NW), NW being the number of waves the
-// GPU holds at once.
-// A worker's share cuts the pair list into segments; for each segment the
-// worker either writes the finished output (it holds the whole pair) or a
-// partial (m, l, o) to slot (pair + w), and the worker holding a pair's first
-// tile records which workers cover the pair (every pair's record is rewritten
-// on every call: empty sequences' pairs are marked by the workgroups).  Slots
-// are distinct: along the tile list, pair + worker grows by at least one at
-// every segment start.
+// The work is the list of all 16-token tiles of all sequences, numbered
+// sequence by sequence.  A group of gs waves (gs KV heads of one sequence,
+// one head per wave; the heads are cut into Hkv / gs chunks) is a worker
+// that takes one contiguous, equal share [j T / ng, (j + 1) T / ng) of the
+// T = (Hkv / gs) x (tiles of all sequences) (sequence, chunk, tile) items,
+// so every worker reads the same number of K/V bytes however ragged the
+// context lengths are, and streams its share with the next tiles' loads
+// always in flight.  The waves of a group walk the same tiles side by side,
+// so the gs head runs of one block, which sit next to each other in the
+// [block, head, token, dim] layout (32 KiB of K and of V for 8 heads of 16
+// tokens x 128 dims), are requested together: a random gather of such runs
+// streams faster than one of separate 4 KiB runs.  ng = min(T, the groups
+// the GPU holds at once).
+// A worker's share cuts the (sequence, chunk) list into segments; for each
+// segment every wave of the group either writes its head's finished output
+// (the group holds the whole sequence) or a partial (m, l, o) to slot
+// ((sequence x chunks + chunk + j) gs + wave in group), and the group holding
+// a sequence's first tile records which groups cover it (every record is
+// rewritten on every call: empty sequences' pairs are marked by the
+// workgroups).  Slots are distinct: along the item list, sequence x chunks +
+// chunk + j grows by at least one at every segment start.
 
-// Number of the worker whose share [w T / nw, (w + 1) T / nw) holds tile u.
+constexpr int kBWaves = 8;  // waves of a balanced-split workgroup (one per CU)
+constexpr int kTileBufs = 2;  // K/V tile buffers per wave (tiles in flight + 1)
+constexpr int kBThreads = kBWaves * kWave;
+
+// Number of the worker whose share [j T / n, (j + 1) T / n) holds item u.
 __device__ inline int worker_of(int64_t u, int64_t total, int32_t num_workers) {
   return (int)(((u + 1) * num_workers - 1) / total);
 }
 
 template <int D, int B, int G, bool kAppend>
-__global__ __launch_bounds__(kThreads) void decode_balanced_kernel(
+__global__ __launch_bounds__(kBThreads) void decode_balanced_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     int32_t table_width, const int32_t* __restrict__ context_lens, uint16_t* __restrict__ out,
     int2* __restrict__ meta, float* __restrict__ part_ml, float* __restrict__ part_o,
     int32_t num_seqs, int32_t num_kv_heads, int32_t num_blocks, int32_t max_context_len,
-    int32_t num_workers, float qscale, const uint16_t* __restrict__ k_new,
+    int32_t num_groups, int32_t gs, float qscale, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, uint16_t* k_dst, uint16_t* v_dst) {
   constexpr int DT = D / 16;
   extern __shared__ int32_t sm_dyn[];
-  int32_t* sm_c = sm_dyn;                 // [num_seqs + 1] tiles of one KV head before sequence s
+  int32_t* sm_c = sm_dyn;                 // [num_seqs + 1] tiles of one chunk before sequence s
   int32_t* sm_n = sm_dyn + num_seqs + 1;  // [num_seqs] clamped context lengths
-  __shared__ int32_t sm_scan[kWaves];  // wave totals of the scan
+  __shared__ int32_t sm_scan[kBWaves];    // wave totals of the scan
 
   // Prefix sums of the tile counts (every workgroup computes its own copy).
   {
-    const int per = (num_seqs + kThreads - 1) / kThreads;
+    const int per = (num_seqs + kBThreads - 1) / kBThreads;
     const int i0 = min(num_seqs, (int)threadIdx.x * per);
     const int i1 = min(num_seqs, i0 + per);
     int local = 0;
@@ -741,7 +752,7 @@ __global__ __launch_bounds__(kThreads) void decode_balanced_kernel(
       run += (sm_n[i] + kTile - 1) / kTile;
     }
     // the last thread's running sum is the total (its own sequences included)
-    if (threadIdx.x == kThreads - 1) sm_c[num_seqs] = run;
+    if (threadIdx.x == kBThreads - 1) sm_c[num_seqs] = run;
     __syncthreads();
   }
 
@@ -754,8 +765,8 @@ __global__ __launch_bounds__(kThreads) void decode_balanced_kernel(
   // pairs are marked so that the combine kernel skips them.
   for (int i = blockIdx.x; i < num_seqs; i += gridDim.x) {
     if (sm_n[i] != 0) continue;
-    for (int e = threadIdx.x; e < hq * D; e += kThreads) out[(int64_t)i * hq * D + e] = 0;
-    for (int g = threadIdx.x; g < num_kv_heads; g += kThreads)
+    for (int e = threadIdx.x; e < hq * D; e += kBThreads) out[(int64_t)i * hq * D + e] = 0;
+    for (int g = threadIdx.x; g < num_kv_heads; g += kBThreads)
       meta[(int64_t)i * num_kv_heads + g] = make_int2(-1, -1);
   }
   if constexpr (kAppend) {
@@ -769,7 +780,7 @@ __global__ __launch_bounds__(kThreads) void decode_balanced_kernel(
       if (t < 0) continue;
       const int phys = block_tables[(int64_t)i * table_width + t / B];
       if (phys < 0 || phys >= num_blocks) continue;
-      for (int e = threadIdx.x; e < per_seq; e += kThreads) {
+      for (int e = threadIdx.x; e < per_seq; e += kBThreads) {
         const int which = e / (num_kv_heads * kChunks);
         const int r = e - which * num_kv_heads * kChunks;
         const int g = r / kChunks;
@@ -781,149 +792,165 @@ __global__ __launch_bounds__(kThreads) void decode_balanced_kernel(
       }
     }
   }
-  const int64_t total = (int64_t)num_kv_heads * sm_c[num_seqs];
-  // With fewer tiles than workers only the first `total` workers take one
-  // each: every worker in [0, nw) has a non-empty share, so the workers that
-  // cover a pair are exactly the range between its first and last tile's.
-  const int nw = (int)min((int64_t)num_workers, total);
-  const int w = blockIdx.x * kWaves + wave;
-  if (w >= nw) return;  // no barrier follows: the waves are independent from here
-  const int64_t u0 = (int64_t)w * total / nw;
-  const int64_t u1 = (int64_t)(w + 1) * total / nw;
+  const int chunks = num_kv_heads / gs;
+  const int64_t total = (int64_t)chunks * sm_c[num_seqs];
+  // With fewer items than groups only the first `total` groups take one
+  // each: every group in [0, ng) has a non-empty share, so the groups that
+  // cover a sequence's chunk are exactly the range between its first and
+  // last item's.
+  const int ng = (int)min((int64_t)num_groups, total);
+  const int wg = blockIdx.x * kBWaves + wave;  // gs divides kBWaves: groups stay in a workgroup
+  const int j = wg / gs;                       // this wave's group (worker)
+  const int hi = wg - j * gs;                  // its head within the chunk
+  if (j >= ng) return;  // no barrier follows: the waves are independent from here
+  const int64_t u0 = (int64_t)j * total / ng;
+  const int64_t u1 = (int64_t)(j + 1) * total / ng;
 
-  // A tile's place: sequence, KV head, tile index in the pair, the pair's tile
-  // count and the sequence's length (all wave-uniform).
+  // An item's place: sequence, chunk, tile index in the chunk's pair, the
+  // sequence's tile count and length (all wave-uniform).  This wave's head is
+  // g = c gs + hi.
   struct Pos {
-    int s, g, tile, nt, n;
+    int s, c, tile, nt, n;
   };
   auto seq_info = [&](Pos& x) {
     x.nt = __builtin_amdgcn_readfirstlane(sm_c[x.s + 1] - sm_c[x.s]);
     x.n = __builtin_amdgcn_readfirstlane(sm_n[x.s]);
   };
   auto pos_of = [&](int64_t u) {
-    // The last sequence whose first tile is <= u: the first tiles do not
+    // The last sequence whose first item is <= u: the first items do not
     // decrease, so it is one less than the number of sequences starting at or
     // before u, counted 64 at a time with a ballot.
     int count = 0;
     for (int c = 0; c < num_seqs; c += kWave) {
-      const int j = c + lane;
-      const bool at_or_before = j < num_seqs && (int64_t)num_kv_heads * sm_c[j] <= u;
+      const int jj = c + lane;
+      const bool at_or_before = jj < num_seqs && (int64_t)chunks * sm_c[jj] <= u;
       count += __builtin_popcountll(__builtin_amdgcn_ballot_w64(at_or_before));
     }
     Pos x;
     x.s = __builtin_amdgcn_readfirstlane(count - 1);
     seq_info(x);
-    const int64_t r = u - (int64_t)num_kv_heads * __builtin_amdgcn_readfirstlane(sm_c[x.s]);
-    x.g = (int)(r / x.nt);
-    x.tile = (int)(r - (int64_t)x.g * x.nt);
+    const int64_t r = u - (int64_t)chunks * __builtin_amdgcn_readfirstlane(sm_c[x.s]);
+    x.c = (int)(r / x.nt);
+    x.tile = (int)(r - (int64_t)x.c * x.nt);
     return x;
   };
-  auto next = [&](Pos x) {  // only called for tiles before u1, so the result is a tile
+  auto next = [&](Pos x) {  // only called for items before u1, so the result is an item
     if (++x.tile < x.nt) return x;
     x.tile = 0;
-    if (++x.g < num_kv_heads) return x;
-    x.g = 0;
+    if (++x.c < chunks) return x;
+    x.c = 0;
     do {
       ++x.s;
     } while (__builtin_amdgcn_readfirstlane(sm_c[x.s + 1]) == __builtin_amdgcn_readfirstlane(sm_c[x.s]));
     seq_info(x);
     return x;
   };
-  // Block-table entry of this lane's row of tile x (a valid entry of the
-  // sequence's row even for rows past its end).
-  // The tile of the pair processed at place x.tile.  Pair (s, g)'s order is
-  // rotated by g nt / Hkv tiles, so the workers on the KV heads of one
-  // sequence, which move through their pairs side by side, do not read the
-  // head runs of the same physical blocks at the same moment.
+  // The tile of the sequence processed at place x.tile.  The chunks of one
+  // sequence start their tiles at different places (rotated by c nt /
+  // chunks), so groups on different chunks of one sequence, which move
+  // through it side by side, do not read the same physical blocks at the
+  // same moment; the waves of one group do, on purpose.
   auto ptile = [&](const Pos& x) {
-    const int r = x.tile + (x.g * x.nt) / num_kv_heads;
+    const int r = x.tile + (x.c * x.nt) / chunks;
     return r >= x.nt ? r - x.nt : r;
   };
+  // Block-table entry of this lane's row of tile x (a valid entry of the
+  // sequence's row even for rows past its end).
   auto table_entry = [&](const Pos& x) {
     const int t = min(ptile(x) * kTile + col, x.n - 1);
     return block_tables[(int64_t)x.s * table_width + t / B];
   };
   const uint16_t* safe = q + 8 * grp;
   // With kAppend the row of position n - 1 (the token appended this step)
-  // comes from k_new / v_new [num_seqs, Hkv, D] instead of the cache, and
-  // step() stores it into the cache slot: the same bits either way.
+  // comes from k_new / v_new [num_seqs, Hkv, D] instead of the cache (the
+  // prologue stored it into the cache slot: the same bits either way).
   auto load_tile = [&](const Pos& x, int phys, bool live, KVTile<D>& kv) {
     const int t = ptile(x) * kTile + col;
+    const int g = x.c * gs + hi;
     const uint16_t* kr = nullptr;
     const uint16_t* vr = nullptr;
     if constexpr (kAppend) {
-      const int64_t nrow = ((int64_t)x.s * num_kv_heads + x.g) * D + 8 * grp;
+      const int64_t nrow = ((int64_t)x.s * num_kv_heads + g) * D + 8 * grp;
       kr = t == x.n - 1 ? k_new + nrow : nullptr;
       vr = t == x.n - 1 ? v_new + nrow : nullptr;
     }
-    load_kv<D, B>(kv, k_cache, v_cache, safe, live && t < x.n, phys, t, x.g, num_kv_heads,
+    load_kv<D, B>(kv, k_cache, v_cache, safe, live && t < x.n, phys, t, g, num_kv_heads,
                   num_blocks, grp, kr, vr);
   };
+  auto qrow = [&](const Pos& x) { return q + ((int64_t)x.s * hq + (x.c * gs + hi) * G) * D; };
 
   MfmaAttn<D, G> at;
   at.init(col, grp);
-  int64_t seg_u0 = u0;  // first tile of the current segment
+  int64_t seg_u0 = u0;  // first item of the current segment
 
-  // Update with tile u (place x); at the end of a segment write its result
-  // and prepare for the next pair (place nx).
+  // Update with item u (place x); at the end of a segment write its result
+  // and prepare for the next (sequence, chunk) (place nx).
   auto step = [&](const Pos& x, int64_t u, KVTile<D>& kv, const Pos& nx) {
     at.update(kv, min(kTile, x.n - ptile(x) * kTile), qscale, grp);
     if (x.tile + 1 < x.nt && u + 1 < u1) return;
-    const int64_t pair_u0 = (int64_t)num_kv_heads * sm_c[x.s] + (int64_t)x.g * x.nt;
-    const int pair = x.s * num_kv_heads + x.g;
+    const int64_t pair_u0 = (int64_t)chunks * sm_c[x.s] + (int64_t)x.c * x.nt;
+    const int g = x.c * gs + hi;
+    const int pair = x.s * num_kv_heads + g;
     const bool first = seg_u0 == pair_u0;
     const bool whole = first && u + 1 == pair_u0 + x.nt;
     const float l = rows_sum(at.l);
     if (col < G) {
-      const int64_t row = (int64_t)x.s * hq + x.g * G + col;
+      const int64_t row = (int64_t)x.s * hq + g * G + col;
       if (whole) {
 #pragma unroll
-        for (int j = 0; j < DT; ++j) {
+        for (int jj = 0; jj < DT; ++jj) {
           uint2 v;
-          v.x = (uint32_t)f32_to_bf16_rne(at.o[j][0] / l) |
-                ((uint32_t)f32_to_bf16_rne(at.o[j][1] / l) << 16);
-          v.y = (uint32_t)f32_to_bf16_rne(at.o[j][2] / l) |
-                ((uint32_t)f32_to_bf16_rne(at.o[j][3] / l) << 16);
-          *reinterpret_cast<uint2*>(out + row * D + 16 * j + 4 * grp) = v;
+          v.x = (uint32_t)f32_to_bf16_rne(at.o[jj][0] / l) |
+                ((uint32_t)f32_to_bf16_rne(at.o[jj][1] / l) << 16);
+          v.y = (uint32_t)f32_to_bf16_rne(at.o[jj][2] / l) |
+                ((uint32_t)f32_to_bf16_rne(at.o[jj][3] / l) << 16);
+          *reinterpret_cast<uint2*>(out + row * D + 16 * jj + 4 * grp) = v;
         }
       } else {
-        const int64_t slot = ((int64_t)pair + w) * G + col;
+        const int64_t slot = (((int64_t)x.s * chunks + x.c + j) * gs + hi) * G + col;
 #pragma unroll
-        for (int j = 0; j < DT; ++j)
-          *reinterpret_cast<float4*>(part_o + slot * D + 16 * j + 4 * grp) =
-              make_float4(at.o[j][0], at.o[j][1], at.o[j][2], at.o[j][3]);
+        for (int jj = 0; jj < DT; ++jj)
+          *reinterpret_cast<float4*>(part_o + slot * D + 16 * jj + 4 * grp) =
+              make_float4(at.o[jj][0], at.o[jj][1], at.o[jj][2], at.o[jj][3]);
         if (grp == 0) *reinterpret_cast<float2*>(part_ml + slot * 2) = make_float2(at.m, l);
       }
     }
     if (first && lane == 0)
-      meta[pair] = make_int2(w, worker_of(pair_u0 + x.nt - 1, total, nw));
+      meta[pair] = make_int2(j, worker_of(pair_u0 + x.nt - 1, total, ng));
     if (u + 1 < u1) {
       at.reset();
-      at.load_q(q + ((int64_t)nx.s * hq + nx.g * G) * D, col, grp);
+      at.load_q(qrow(nx), col, grp);
       seg_u0 = u + 1;
     }
   };
 
-  // Pipeline: the table entry of tile u + 2 and the K/V of tile u + 1 are in
-  // flight while tile u is processed; two tile buffers in turn, with the tile
-  // count padded to an even number (a dummy tile) so the loop has one exit.
-  Pos pa = pos_of(u0);
-  at.load_q(q + ((int64_t)pa.s * hq + pa.g * G) * D, col, grp);
-  Pos pb = u0 + 1 < u1 ? next(pa) : pa;
-  int ph_b = table_entry(pb);
-  KVTile<D> ta, tb;
-  load_tile(pa, table_entry(pa), true, ta);
-  for (int64_t u = u0; u < u1; u += 2) {
-    const Pos pc = u + 2 < u1 ? next(pb) : pb;
-    const int ph_c = table_entry(pc);
-    load_tile(pb, ph_b, u + 1 < u1, tb);
-    step(pa, u, ta, pb);
-    const Pos pd = u + 3 < u1 ? next(pc) : pc;
-    ph_b = table_entry(pd);
-    load_tile(pc, ph_c, u + 2 < u1, ta);
-    if (u + 1 < u1) step(pb, u + 1, tb, pc);
-    pa = pc;
-    pb = pd;
+  // Pipeline over kTileBufs tile buffers: while item u is processed, the K/V
+  // of items u + 1 .. u + kTileBufs - 1 and the table entry of the item after
+  // them are in flight.  The item count is padded to a multiple of kTileBufs
+  // (dummy items load a safe row and are not processed) so the loop has one
+  // exit and the compiler's load counting stays exact across the back edge.
+  // p[f] holds the place of item u + f at the top of each round; each step
+  // replaces its own place with that of the item kTileBufs later.
+  constexpr int NBF = kTileBufs;
+  Pos p[NBF];
+  KVTile<D> t[NBF];
+  p[0] = pos_of(u0);
+  at.load_q(qrow(p[0]), col, grp);
+#pragma unroll
+  for (int f = 1; f < NBF; ++f) p[f] = u0 + f < u1 ? next(p[f - 1]) : p[f - 1];
+#pragma unroll
+  for (int f = 0; f < NBF - 1; ++f) load_tile(p[f], table_entry(p[f]), u0 + f < u1, t[f]);
+  int ph = table_entry(p[NBF - 1]);  // entry of the next item to load
+  for (int64_t u = u0; u < u1; u += NBF) {
+#pragma unroll
+    for (int f = 0; f < NBF; ++f) {
+      const int lb = (f + NBF - 1) % NBF;  // buffer (and place) of item u + f + NBF - 1
+      load_tile(p[lb], ph, u + f + NBF - 1 < u1, t[lb]);
+      const Pos pn = u + f + NBF < u1 ? next(p[lb]) : p[lb];
+      ph = table_entry(pn);
+      if (u + f < u1) step(p[f], u + f, t[f], p[(f + 1) % NBF]);
+      p[f] = pn;
+    }
   }
 }
 
@@ -959,20 +986,22 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(
 // several workers are combined here, in worker order,
 // out = sum_w o_w 2^(m_w - m*) / sum_w L_w 2^(m_w - m*).  Pairs finished by a
 // single worker, and pairs of empty sequences, are left alone.  Contributors
-// are taken 64 at a time: lane j fetches contributor j's (m, L), the group's
-// maximum and weighted sum come from wave reductions, and each lane then
-// folds its D / 64 output dims of up to kChunk contributors, fetched with
-// independent loads (8 at a time for pairs of at most 8 workers), so a pair
-// split over up to kChunk workers costs one round trip after the record of
-// its workers.  Four such waves share a
+// are taken 64 at a time: lane j fetches contributor j's (m, L) while every
+// lane fetches its D / 64 output dims of the group's first kFirst
+// contributors; the group's maximum and weighted sum come from wave
+// reductions, then each lane folds its dims, so a pair split over up to
+// kFirst workers costs one round trip after the record of its workers (the
+// output dims of further contributors follow kChunk at a time).  Four such waves share a
 // workgroup: dispatching one-wave workgroups costs about as much as the whole
 // combine.
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void decode_balanced_reduce_kernel(
     uint16_t* __restrict__ out, const int2* __restrict__ meta, const float* __restrict__ part_ml,
-    const float* __restrict__ part_o, int32_t num_pairs, int32_t num_workers) {
+    const float* __restrict__ part_o, int32_t num_pairs, int32_t num_kv_heads, int32_t num_workers,
+    int32_t gs) {
   constexpr int DPL = D / kWave;  // dims per lane
-  constexpr int kChunk = 32;
+  constexpr int kFirst = 8;       // contributors fetched with the (m, L) of their group
+  constexpr int kChunk = 32;      // contributors fetched per later round
   static_assert(DPL * kWave == D, "head_dim must be a multiple of 64");
   const int unit = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   if (unit >= num_pairs * G) return;
@@ -983,49 +1012,61 @@ __global__ __launch_bounds__(kThreads) void decode_balanced_reduce_kernel(
   const int wa = max(mt.x, 0), wb = min(mt.y, num_workers - 1);
   if (mt.x < 0 || wa >= wb) return;
   const int nseg = wb - wa + 1;
-  const float* ml = part_ml + (((int64_t)pair + wa) * G + h) * 2;  // worker k at ml[k * 2 G]
-  const float* po = part_o + (((int64_t)pair + wa) * G + h) * D + lane * DPL;
+  // The pair (sequence s, KV head g) is item chunk pc = s chunks + g / gs of
+  // the work list; worker k wrote its partial to slot (pc + k) gs + g % gs.
+  const int s = pair / num_kv_heads;
+  const int g = pair - s * num_kv_heads;
+  const int64_t pc = (int64_t)s * (num_kv_heads / gs) + g / gs;
+  const int64_t slot0 = (pc + wa) * gs + g % gs;
+  const int64_t stride = (int64_t)gs * G;  // rows between consecutive workers' slots
+  const float* ml = part_ml + (slot0 * G + h) * 2;  // worker wa + k at ml[k * 2 stride]
+  const float* po = part_o + (slot0 * G + h) * D + lane * DPL;
   float M = -INFINITY, L = 0.0f, O[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) O[e] = 0.0f;
   for (int k0 = 0; k0 < nseg; k0 += kWave) {
     const int ng = min(kWave, nseg - k0);  // contributors in this group
     const bool mine = lane < ng;
-    const float2 v = mine ? *reinterpret_cast<const float2*>(ml + (int64_t)(k0 + lane) * 2 * G)
-                          : make_float2(-INFINITY, 0.0f);
+    // Unpredicated loads with clamped indices (a lane past the group re-reads
+    // the last contributor and its factor is zero), the first kFirst
+    // contributors' output dims issued with the (m, L) loads in one block,
+    // before any of them is waited for.
+    float2 v = *reinterpret_cast<const float2*>(ml + (int64_t)(k0 + min(lane, ng - 1)) * 2 * stride);
+    auto fetch = [&](auto& ov, int c0) {
+      constexpr int kc = sizeof(ov) / sizeof(ov[0]);
+#pragma unroll
+      for (int c = 0; c < kc; ++c) {
+        const int64_t k = k0 + min(c0 + c, ng - 1);
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) ov[c][e] = po[k * stride * D + e];
+      }
+    };
+    float ov0[kFirst][DPL];
+    fetch(ov0, 0);
+    if (!mine) v = make_float2(-INFINITY, 0.0f);
     const float cm = fmaxf(M, group_max<kWave>(v.x));
     const float a = M == -INFINITY ? 0.0f : exp2f(M - cm);  // rescales what came before
     const float f = mine ? exp2f(v.x - cm) : 0.0f;          // lane j: contributor k0 + j's factor
     L = fmaf(L, a, group_sum<kWave>(v.y * f));
 #pragma unroll
     for (int e = 0; e < DPL; ++e) O[e] *= a;
-    // Output dims of kc contributors at a time (kc = 8 when the group is that
-    // small, else 32): the loads of a chunk are independent, and a small
-    // group does not pay for 32 loads.
-    auto fold = [&](auto kc_tag) {
-      constexpr int kc = decltype(kc_tag)::value;
-      for (int c0 = 0; c0 < ng; c0 += kc) {
-        float ov[kc][DPL];
+    auto add = [&](const auto& ov, int c0) {
+      constexpr int kc = sizeof(ov) / sizeof(ov[0]);
 #pragma unroll
-        for (int c = 0; c < kc; ++c) {
-          const int64_t k = k0 + min(c0 + c, ng - 1);
+      for (int c = 0; c < kc; ++c) {
+        // contributors past the group are selected out, not multiplied by 0
+        const float fc = __int_as_float(
+            __builtin_amdgcn_readlane(__float_as_int(f), min(c0 + c, kWave - 1)));
 #pragma unroll
-          for (int e = 0; e < DPL; ++e) ov[c][e] = po[k * G * D + e];
-        }
-#pragma unroll
-        for (int c = 0; c < kc; ++c) {
-          if (c0 + c < ng) {
-            const float fc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), c0 + c));
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) O[e] = fmaf(ov[c][e], fc, O[e]);
-          }
-        }
+        for (int e = 0; e < DPL; ++e) O[e] = c0 + c < ng ? fmaf(ov[c][e], fc, O[e]) : O[e];
       }
     };
-    if (ng <= 8)
-      fold(std::integral_constant<int, 8>{});
-    else
-      fold(std::integral_constant<int, kChunk>{});
+    add(ov0, 0);
+    for (int c0 = kFirst; c0 < ng; c0 += kChunk) {
+      float ov[kChunk][DPL];
+      fetch(ov, c0);
+      add(ov, c0);
+    }
     M = cm;
   }
   uint16_t* orow = out + ((int64_t)pair * G + h) * D + lane * DPL;
@@ -1038,14 +1079,27 @@ __global__ __launch_bounds__(kThreads) void decode_balanced_reduce_kernel(
 constexpr int kWorkerWavesPerSimd = 2;  // the balanced kernel's occupancy (VGPR-bound)
 // Static LDS of the balanced kernel (the wave totals of its scan, sm_scan);
 // the dynamic part is (2 num_seqs + 1) int32 of prefix sums and lengths.
-constexpr int kBalancedStaticLds = kWaves * (int)sizeof(int32_t);
+constexpr int kBalancedStaticLds = kBWaves * (int)sizeof(int32_t);
+// Balanced-split workgroups resident on one CU (kBWaves waves each).
+constexpr int kBalancedWgPerCu = 4 * kWorkerWavesPerSimd / kBWaves;
+static_assert(kBalancedWgPerCu >= 1, "a balanced workgroup must fit one CU");
+
+// Waves of one balanced-split worker group: the largest power of two up to
+// kBWaves that divides the KV head count (the group's waves take that many
+// heads of one sequence).
+int32_t group_size(int32_t num_kv_heads) {
+  int32_t gs = kBWaves;
+  while (num_kv_heads % gs) gs /= 2;
+  return gs;
+}
 
 // How one call is split and where its workspace pieces go.
 struct Plan {
   bool balanced;
   int32_t parts;    // split-context: partitions per sequence
   int32_t ps;       // split-context: tokens per partition
-  int32_t workers;  // balanced: workers (waves)
+  int32_t workers;  // balanced: waves
+  int32_t gs;       // balanced: waves per worker group
   size_t meta_off, ml_off, o_off, bytes;
 };
 
@@ -1054,9 +1108,9 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // What the balanced split needs to know about the current device: its
 // workers (the waves it holds at once: CUs x 4 SIMDs x kWorkerWavesPerSimd)
 // and the most sequences whose prefix sums and lengths fit the LDS one of its
-// workgroups may use.  The grid puts kWorkerWavesPerSimd workgroups on every
-// CU, so a workgroup may use a 1 / kWorkerWavesPerSimd share of the CU's LDS
-// (and no more than the per-workgroup maximum).
+// workgroups may use.  The grid puts kBalancedWgPerCu workgroups on every CU,
+// so a workgroup may use that share of the CU's LDS (and no more than the
+// per-workgroup maximum).
 struct DeviceLimits {
   int32_t workers;
   int32_t max_seqs;
@@ -1081,7 +1135,7 @@ int device_limits(DeviceLimits* out) {
     e = hipDeviceGetAttribute(&lds_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
   if (e != hipSuccess || cus <= 0 || lds_cu <= 0 || lds_block <= 0)
     return pkv__fail(PKV_EHIP, "device attributes: %s", hipGetErrorString(e));
-  const int budget = std::min(lds_block, lds_cu / kWorkerWavesPerSimd);
+  const int budget = std::min(lds_block, lds_cu / kBalancedWgPerCu);
   DeviceLimits d;
   d.workers = cus * 4 * kWorkerWavesPerSimd;
   d.max_seqs = std::max(0, (budget - kBalancedStaticLds - (int)sizeof(int32_t)) /
@@ -1109,6 +1163,7 @@ int make_plan(const pkv_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
       const size_t slots = (pairs + (size_t)nw) * G;
       pl->balanced = true;
       pl->workers = nw;
+      pl->gs = group_size(c->num_kv_heads);
       pl->meta_off = 0;
       pl->ml_off = align256(pairs * sizeof(int2));
       pl->o_off = pl->ml_off + align256(slots * 2 * sizeof(float));
@@ -1167,22 +1222,22 @@ int launch(const LaunchArgs& a) {
   if constexpr (E::bytes == 2) {
     if (a.plan.balanced) {
       const size_t lds = (size_t)(2 * a.num_seqs + 1) * sizeof(int32_t);
+      const int32_t groups = a.plan.workers / a.plan.gs;
+      const dim3 grid((uint32_t)(a.plan.workers / kBWaves));
       if (a.k_new)
-        hipLaunchKernelGGL((decode_balanced_kernel<D, B, G, true>),
-                           dim3((uint32_t)(a.plan.workers / kWaves)), dim3(kThreads), lds,
+        hipLaunchKernelGGL((decode_balanced_kernel<D, B, G, true>), grid, dim3(kBThreads), lds,
                            a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
                            (const uint16_t*)a.v_cache, a.block_tables, a.width, a.context_lens,
                            (uint16_t*)a.out, a.meta, a.part_ml, a.part_o, a.num_seqs,
-                           a.num_kv_heads, a.num_blocks, a.max_context_len, a.plan.workers,
+                           a.num_kv_heads, a.num_blocks, a.max_context_len, groups, a.plan.gs,
                            a.qscale, (const uint16_t*)a.k_new, (const uint16_t*)a.v_new,
                            (uint16_t*)a.k_cache, (uint16_t*)a.v_cache);
       else
-        hipLaunchKernelGGL((decode_balanced_kernel<D, B, G, false>),
-                           dim3((uint32_t)(a.plan.workers / kWaves)), dim3(kThreads), lds,
+        hipLaunchKernelGGL((decode_balanced_kernel<D, B, G, false>), grid, dim3(kBThreads), lds,
                            a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
                            (const uint16_t*)a.v_cache, a.block_tables, a.width, a.context_lens,
                            (uint16_t*)a.out, a.meta, a.part_ml, a.part_o, a.num_seqs,
-                           a.num_kv_heads, a.num_blocks, a.max_context_len, a.plan.workers,
+                           a.num_kv_heads, a.num_blocks, a.max_context_len, groups, a.plan.gs,
                            a.qscale, nullptr, nullptr, nullptr, nullptr);
       int rc = check_launch("decode_balanced");
       if (rc) return rc;
@@ -1190,7 +1245,8 @@ int launch(const LaunchArgs& a) {
       hipLaunchKernelGGL((decode_balanced_reduce_kernel<D, G>),
                          dim3((uint32_t)((units + kWaves - 1) / kWaves)), dim3(kThreads), 0,
                          a.stream, (uint16_t*)a.out, (const int2*)a.meta, (const float*)a.part_ml,
-                         (const float*)a.part_o, a.num_seqs * a.num_kv_heads, a.plan.workers);
+                         (const float*)a.part_o, a.num_seqs * a.num_kv_heads, a.num_kv_heads,
+                         groups, a.plan.gs);
       return check_launch("decode_balanced_reduce");
     }
   }
