@@ -86,6 +86,10 @@ def parse():
     ap.add_argument("--unfused", action="store_true",
                     help="run paged_kv_write and the decode as two launches instead of the fused "
                          "append + decode")
+    ap.add_argument("--gather-probe", action="store_true",
+                    help="instead of the benchmark, time pkv_measure_gather on the workload's "
+                         "own (block, KV head) runs in the decode's share rule, with no "
+                         "arithmetic, in several orders (the memory-system ceiling of the decode)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the benchmark, time a plain device copy of this many MiB "
                          "(the reference kernel for HBM counter calibration and the copy ceiling)")
@@ -324,7 +328,112 @@ def to_dev(a, torch):
     return torch.from_numpy(a).cuda()
 
 
-def cpu_baseline(wl: Workload, min_s: float = 10.0, max_s: float = 20.0):
+# ------------------------------------------------------------ CPU baseline
+#
+# The oracle on the host: (i) one process, numpy/BLAS limited to one thread;
+# (ii) a pool of processes, one sequence per task, on the host cores the job
+# may use (at most 16).  The pool is forked when bench.py starts, before torch
+# or the HIP library is loaded, and reads the inputs from shared memory.
+
+CPU_POOL_MAX = 16
+
+
+def cpu_cores() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, CPU_POOL_MAX))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def start_cpu_pool():
+    import multiprocessing as mp
+    n = cpu_cores()
+    return mp.get_context("fork").Pool(n), n
+
+
+_SHM = {}
+
+
+def _attach(spec):
+    """numpy views of shared-memory arrays {name: (shm name, shape, dtype)}."""
+    from multiprocessing import resource_tracker, shared_memory
+    out = {}
+    for k, (nm, shape, dt) in spec.items():
+        if nm not in _SHM:
+            _SHM[nm] = shared_memory.SharedMemory(name=nm)
+            # attaching registers the segment for removal at this process's
+            # exit; the parent owns and removes it
+            resource_tracker.unregister(_SHM[nm]._name, "shared_memory")
+        out[k] = np.ndarray(shape, dtype=np.dtype(dt), buffer=_SHM[nm].buf)
+    return out
+
+
+def _oracle_decode_task(task):
+    spec, s_, scale, dtype = task
+    import oracle
+    from threadpoolctl import threadpool_limits
+    a = _attach(spec)
+    with threadpool_limits(1):
+        oracle.paged_attention_decode(a["q"], a["k"], a["v"], a["tables"], a["ctx"], scale, dtype,
+                                      seqs=[s_])
+    return s_
+
+
+def _oracle_prefill_task(task):
+    spec, s_, scale, dtype = task
+    import oracle
+    from threadpoolctl import threadpool_limits
+    a = _attach(spec)
+    with threadpool_limits(1):
+        oracle.paged_attention_prefill(a["q"], a["k"], a["v"], a["tables"], a["ctx"], a["qsl"],
+                                       scale, dtype, seqs=[s_])
+    return s_
+
+
+def pool_run(pool, arrays: dict, fn, seqs, weight, scale, dtype, min_s: float = 8.0):
+    """Run fn over sequences `seqs` (heaviest first) on the pool, whole passes
+    until at least min_s seconds; returns (tasks done, weight done, seconds)."""
+    from multiprocessing import shared_memory
+    shms, spec = [], {}
+    try:
+        for k, arr in arrays.items():
+            arr = np.ascontiguousarray(arr)
+            shm = shared_memory.SharedMemory(create=True, size=max(arr.nbytes, 1))
+            shms.append(shm)
+            np.ndarray(arr.shape, dtype=arr.dtype, buffer=shm.buf)[...] = arr
+            spec[k] = (shm.name, arr.shape, arr.dtype.str)
+        order = sorted(seqs, key=lambda x: -weight[x])
+        tasks = [(spec, int(x), scale, dtype) for x in order]
+        pool.map(fn, tasks[:CPU_POOL_MAX], chunksize=1)  # untimed: workers attach the inputs
+        done = wsum = 0
+        t0 = time.perf_counter()
+        while True:
+            for x in pool.imap_unordered(fn, tasks, chunksize=1):
+                done += 1
+                wsum += weight[x]
+            if time.perf_counter() - t0 >= min_s:
+                break
+        return done, wsum, time.perf_counter() - t0
+    finally:
+        for shm in shms:
+            shm.close()
+            shm.unlink()
+
+
+def cpu_baseline(wl: Workload, pool=None, pool_cores: int = 0, min_s: float = 10.0,
+                 max_s: float = 20.0):
     """fp64 oracle on one host core: step 0's whole batch (every sequence, all
     heads), decoded again and again until at least ``min_s`` seconds of CPU work
     (stopping mid-batch at ``max_s``); GB/s counts the K/V bytes decoded."""
@@ -361,12 +470,24 @@ def cpu_baseline(wl: Workload, min_s: float = 10.0, max_s: float = 20.0):
         m.step(wl.seq_ids)
         m.build_tables(wl.seq_ids, wl.width + 8)
     alloc_us = (time.perf_counter() - ta) / 20 * 1e6
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"fp64 decode of step 0's batch ({sh.num_seqs} sequences, all {sh.num_q_heads} "
-                      f"heads) repeated: {done} sequence decodes ({reps} whole batches) in {dt:.1f} s, "
-                      f"numpy/BLAS limited to 1 thread",
-            "seqs_per_s": done / dt,
-            "allocator_us_per_step": round(alloc_us, 1)}
+    res = {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"fp64 decode of step 0's batch ({sh.num_seqs} sequences, all {sh.num_q_heads} "
+                     f"heads) repeated: {done} sequence decodes ({reps} whole batches) in {dt:.1f} s, "
+                     f"numpy/BLAS limited to 1 thread",
+           "seqs_per_s": done / dt,
+           "cpu_model": cpu_model(),
+           "allocator_us_per_step": round(alloc_us, 1)}
+    if pool is not None:
+        kv_row = {x: int(st["ctx"][x]) * row_bytes for x in range(sh.num_seqs)}
+        n, b, el = pool_run(pool, {"q": st["q"], "k": kc, "v": vc, "tables": st["tables"],
+                                   "ctx": st["ctx"]},
+                            _oracle_decode_task, range(sh.num_seqs), kv_row, sh.scale, sh.dtype)
+        res["multicore"] = {"value": round(b / el / 1e9, 4), "unit": "GB/s", "cores": pool_cores,
+                            "seqs_per_s": round(n / el, 3),
+                            "sample": f"the same batch on a pool of {pool_cores} processes (one "
+                                      f"sequence per task, heaviest first, 1 BLAS thread each): "
+                                      f"{n} sequence decodes in {el:.1f} s"}
+    return res
 
 
 def copy_probe(mib: int, reps: int) -> None:
@@ -393,6 +514,92 @@ def copy_probe(mib: int, reps: int) -> None:
           flush=True)
 
 
+def gather_probe(args, torch, pkv) -> None:
+    """Time the gather of the workload's K/V runs alone (pkv_measure_gather),
+    with the decode's workers, share rule and cold pool rotation:
+
+      pair order     (sequence, KV head, block): each wave streams one head's
+                     4 KiB runs of scattered blocks
+      group order    the balanced decode's assignment: the (sequence, block)
+                     items cut into equal shares of a group of 8 waves, wave i
+                     reading KV head i of each item, so a block's head runs are
+                     requested by the group's waves together (the few items
+                     past the last whole share are left out)
+      block order    (sequence, block, KV head): one wave reads a block's head
+                     runs one after another (32 KiB of K and of V at 8 heads x
+                     16 x 128 bf16)
+      address order  the same runs sorted by address
+      whole pool     every run of the pool in address order (a sequential read)
+
+    Each launch is timed with HIP events on the stream; the median of
+    ``--steps`` launches after ``--warmup`` is reported."""
+    wl = Workload(args.workload, args.block_size, 1)
+    sh = wl.shape
+    st = wl.steps[0]
+    B, H = sh.block_size, sh.num_kv_heads
+    nblk = -(-st["ctx"].astype(np.int64) // B)
+    pair_runs, block_runs = [], []
+    for s_, n in enumerate(nblk):
+        ids = st["tables"][s_, :n].astype(np.int64) * H
+        pair_runs.append((ids[None, :] + np.arange(H)[:, None]).reshape(-1))
+        block_runs.append((ids[:, None] + np.arange(H)[None, :]).reshape(-1))
+    pair_runs = np.concatenate(pair_runs).astype(np.int32)
+    props = torch.cuda.get_device_properties(0)
+    workers = props.multi_processor_count * 4 * 2      # the balanced decode's waves
+    gs = 8
+    while H % gs:
+        gs //= 2
+    # the kernel's item list: (sequence, head chunk, block), as the run of the
+    # chunk's first head
+    chunk_items = np.concatenate([st["tables"][s_, :n].astype(np.int64) * H + c * gs
+                                  for s_, n in enumerate(nblk) for c in range(H // gs)])
+    ng = workers // gs
+    per = len(chunk_items) // ng
+    shares = chunk_items[: ng * per].reshape(ng, per)
+    group_runs = (shares[:, None, :] + np.arange(gs)[None, :, None]).reshape(-1).astype(np.int32)
+    orders = {"pair": pair_runs, "group": group_runs,
+              "block": np.concatenate(block_runs).astype(np.int32),
+              "address": np.sort(pair_runs),
+              "whole_pool": np.arange(wl.num_blocks * H, dtype=np.int32)}
+    R = args.replicas if args.replicas > 0 else cold_replicas(wl.w.k_cache.nbytes + wl.w.v_cache.nbytes)
+    kcs = [to_dev(wl.w.k_cache, torch) for _ in range(R)]
+    vcs = [to_dev(wl.w.v_cache, torch) for _ in range(R)]
+    sink = torch.zeros(workers, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    run_bytes = B * sh.head_dim * sh.elem_bytes
+    res = {"gather_probe": WORKLOAD_NAMES[args.workload], "replicas": R, "workers": workers,
+           "run_bytes": run_bytes, "statistic": f"median of {args.steps} launches, HIP events",
+           "orders": {}}
+    for name, runs in orders.items():
+        druns = to_dev(runs, torch)
+        nbytes = 2 * len(runs) * run_bytes
+        rec = {"runs": int(len(runs)), "bytes": int(nbytes)}
+        for fl in (1, 3):
+            i = 0
+
+            def launch():
+                nonlocal i
+                pkv.measure_gather(kcs[i % R], vcs[i % R], druns, workers, fl, sink, stream=stream)
+                i += 1
+
+            for _ in range(args.warmup):
+                launch()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+            torch.cuda.synchronize()
+            for a, b in evs:
+                a.record(stream)
+                launch()
+                b.record(stream)
+            torch.cuda.synchronize()
+            us = float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3
+            rec[f"in_flight_{fl}"] = {"us": round(us, 2), "gbps": round(nbytes / us / 1e3, 1),
+                                      "frac_of_8tbps": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4)}
+        res["orders"][name] = rec
+        print(f"[gather] {name}: {rec}", file=sys.stderr, flush=True)
+    print(json.dumps(res), flush=True)
+
+
 def prefill_flops(ctx, qsl, num_q_heads: int, head_dim: int) -> int:
     """Attention flops of a causal prefill: 4 D per (query row, head, key it
     sees) -- 2 D for the logit, 2 D for the weighted value."""
@@ -404,7 +611,7 @@ def prefill_flops(ctx, qsl, num_q_heads: int, head_dim: int) -> int:
     return 4 * head_dim * num_q_heads * pairs
 
 
-def run_prefill(args, torch, pkv):
+def run_prefill(args, torch, pkv, cpu_pool=(None, 0)):
     import datagen
 
     w = datagen.prefill_inputs(block_size=args.block_size or 16)
@@ -485,7 +692,7 @@ def run_prefill(args, torch, pkv):
                      "unique_bytes_per_launch": prefill_unique_bytes(ctx, T, sh)},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_prefill(w, tables, ctx)
+        res["cpu_baseline"] = cpu_baseline_prefill(w, tables, ctx, cpu_pool[0], cpu_pool[1])
     print(json.dumps(res), flush=True)
 
 
@@ -499,7 +706,7 @@ def prefill_unique_bytes(ctx, num_tokens: int, sh) -> int:
     return kv + qo + 4 * blocks
 
 
-def cpu_baseline_prefill(w, tables, ctx, min_s: float = 10.0):
+def cpu_baseline_prefill(w, tables, ctx, pool=None, pool_cores: int = 0, min_s: float = 10.0):
     """fp64 oracle prefill on one host core, one sequence at a time (all its
     heads and rows) until ``min_s`` seconds; TFLOP/s over the same count."""
     import oracle
@@ -518,9 +725,21 @@ def cpu_baseline_prefill(w, tables, ctx, min_s: float = 10.0):
             if time.perf_counter() - t0 >= min_s:
                 break
     el = time.perf_counter() - t0
-    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": f"fp64 prefill of {len(done)} of {sh.num_seqs} sequences (all rows and heads) "
-                      f"in {el:.1f} s, numpy/BLAS limited to 1 thread"}
+    res = {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+           "sample": f"fp64 prefill of {len(done)} of {sh.num_seqs} sequences (all rows and heads) "
+                     f"in {el:.1f} s, numpy/BLAS limited to 1 thread",
+           "cpu_model": cpu_model()}
+    if pool is not None:
+        fl = {x: prefill_flops(ctx[x:x + 1], w.qsl[x:x + 2] - w.qsl[x], sh.num_q_heads, sh.head_dim)
+              for x in range(sh.num_seqs)}
+        n, f, el = pool_run(pool, {"q": w.q, "k": w.k_cache, "v": w.v_cache, "tables": tables,
+                                   "ctx": ctx, "qsl": w.qsl},
+                            _oracle_prefill_task, range(sh.num_seqs), fl, sh.scale, sh.dtype)
+        res["multicore"] = {"value": round(f / el / 1e12, 6), "unit": "TFLOP/s", "cores": pool_cores,
+                            "sample": f"all {sh.num_seqs} sequences on a pool of {pool_cores} "
+                                      f"processes (one sequence per task, heaviest first): {n} "
+                                      f"sequence prefills in {el:.1f} s"}
+    return res
 
 
 def run_swap(args, torch, pkv):
@@ -583,6 +802,23 @@ def main():
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
+    cpu_pool = (None, 0)
+    if (not args.no_cpu_baseline and not args.copy_probe_mib and not args.gather_probe
+            and args.workload != 8):
+        cpu_pool = start_cpu_pool()   # before anything loads the HIP runtime
+    try:
+        run(args, cpu_pool)
+    finally:
+        if cpu_pool[0] is not None:
+            cpu_pool[0].terminate()
+            cpu_pool[0].join()
+
+
+def timed_range(args):
+    return range(args.warmup, args.warmup + args.steps)
+
+
+def run(args, cpu_pool):
     import torch
     import paged_kv_cache_377_amd as pkv
 
@@ -592,8 +828,11 @@ def main():
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib, max(args.steps, 1))
         return
+    if args.gather_probe:
+        gather_probe(args, torch, pkv)
+        return
     if args.workload == 7:
-        run_prefill(args, torch, pkv)
+        run_prefill(args, torch, pkv, cpu_pool)
         return
     if args.workload == 8:
         run_swap(args, torch, pkv)
@@ -670,6 +909,34 @@ def main():
     ev3.record(stream)
     torch.cuda.synchronize()
     dec_avg_ms = ev2.elapsed_time(ev3) / args.steps
+    # The same calls once more, each between its own pair of events (median).
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in timed_range(args)]
+    torch.cuda.synchronize()
+    for (a, b), i in zip(evs, timed_range(args)):
+        a.record(stream)
+        decode(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    dec_med_ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+    # Host-to-device upload of one step's inputs from pinned host memory (the
+    # allocator's tables, lengths and slots, the queries and the new K/V),
+    # which the timed steps find already resident.
+    st0 = wl.steps[0]
+    host_in = [torch.from_numpy(np.ascontiguousarray(st0[k])).pin_memory()
+               for k in ("tables", "ctx", "slots", "q", "k", "v")]
+    dev_in = [torch.empty_like(h, device="cuda") for h in host_in]
+    ev6, ev7 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev6.record(stream)
+    for _ in range(args.steps):
+        for h, d_ in zip(host_in, dev_in):
+            d_.copy_(h, non_blocking=True)
+    ev7.record(stream)
+    torch.cuda.synchronize()
+    upload_ms = ev6.elapsed_time(ev7) / args.steps
+    upload_bytes = int(sum(h.numel() * h.element_size() for h in host_in))
 
     copy_rec = None
     if wl.copy_pairs is not None and len(wl.copy_pairs):
@@ -720,7 +987,21 @@ def main():
         "event_ms_per_step": round(step_gpu_ms, 4),
         "step_launches": "copy_blocks (when pairs) + fused append/decode" if fused
                          else "copy_blocks (when pairs) + paged_kv_write + decode",
+        "step_scope": "GPU work only: each step's host allocator call and input upload are "
+                      "done before the timed region (allocator_us_per_step and upload_ms "
+                      "measure them; end_to_end_ms_per_step adds them serially)",
+        "timing": {"value": f"wall clock of {args.steps} whole steps after {args.warmup} "
+                            "warm-up steps, synchronize on both sides, no events inside",
+                   "decode_ms": f"mean of {args.steps} decode calls replayed back to back "
+                                "between two HIP events on the launch stream",
+                   "decode_ms_median": f"median of the same {args.steps} calls, each between "
+                                       "its own pair of events",
+                   "cold_caches": f"step i reads pool copy i mod {R}: the other copies stream "
+                                  "at least 4x the 256 MiB Infinity Cache between two uses"},
         "decode_ms": round(dec_avg_ms, 4),
+        "decode_ms_median": round(dec_med_ms, 4),
+        "upload_ms": round(upload_ms, 4),
+        "upload_bytes": upload_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(args.workload, args.block_size,
@@ -748,8 +1029,10 @@ def main():
         a2.step(wl.seq_ids)
         a2.build_tables(wl.seq_ids, wl.width + 8)
     res["allocator_us_per_step"] = round((time.perf_counter() - t1) / 50 * 1e6, 1)
+    res["end_to_end_ms_per_step"] = round(ms_per_step + upload_ms
+                                          + res["allocator_us_per_step"] / 1e3, 4)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl)
+        res["cpu_baseline"] = cpu_baseline(wl, cpu_pool[0], cpu_pool[1])
         res["cpu_baseline"]["value"] = round(res["cpu_baseline"]["value"], 4)
         res["cpu_baseline"]["seqs_per_s"] = round(res["cpu_baseline"]["seqs_per_s"], 3)
     print(json.dumps(res), flush=True)

@@ -26,6 +26,7 @@ from ._lib import (  # noqa: F401
     decode_workspace_bytes,
     header_functions,
     lib,
+    measure_gather,
     paged_attention_decode,
     paged_attention_decode_append,
     paged_attention_decode_noalloc,

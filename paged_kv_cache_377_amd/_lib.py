@@ -19,6 +19,7 @@ import numpy as np
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libpagedkv.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "pagedkv.h")
+HEADERS = [HEADER, os.path.join(os.path.dirname(PKG), "include", "pagedkv_measure.h")]
 
 PKV_OK, PKV_EINVAL, PKV_ENOBLOCKS, PKV_ERANGE, PKV_EHIP, PKV_EUNSUPPORTED = 0, -1, -2, -3, -4, -5
 PKV_F32, PKV_BF16 = 0, 1
@@ -98,6 +99,7 @@ _SIGS = {
     "pkv_host_pool_export": (_i32, [_vp, _vp, _vp, _vp]),
     "pkv_swap_blocks": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _P(CacheDesc), _vp, _i32, _vp]),
     "pkv_last_error": (ctypes.c_char_p, []),
+    "pkv_measure_gather": (_i32, [_vp, _vp, _P(CacheDesc), _vp, _i64, _i32, _i32, _vp, _vp]),
 }
 
 _lib = None
@@ -119,10 +121,12 @@ def lib() -> ctypes.CDLL:
 
 
 def header_functions() -> List[str]:
-    """Names of the functions include/pagedkv.h declares."""
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+    """Names of the functions the headers under include/ declare."""
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def _check(rc: int):
@@ -378,6 +382,21 @@ def swap_blocks(dst_k, dst_v, src_k, src_v, pairs, stream=None) -> None:
                                  _ptr(src_k, True), _ptr(src_v, True),
                                  src_k.shape[0], ctypes.byref(desc), _ptr(pairs, True),
                                  pairs.shape[0] if pairs.numel() else 0, _stream(stream)))
+
+
+def measure_gather(k_pool, v_pool, runs, num_workers: int, runs_in_flight: int, sink,
+                   stream=None) -> None:
+    """Read (block, KV head) runs ``runs`` ([n] int32, device) of both pools,
+    ``num_workers`` waves in equal contiguous shares, no arithmetic (the
+    memory-system time of the decode's gather); ``sink``: [num_workers] int32."""
+    torch = _torch()
+    _check_pools(k_pool, v_pool)
+    if runs.dtype != torch.int32 or sink.dtype != torch.int32 or sink.numel() < num_workers:
+        raise PagedKVError(PKV_EINVAL, "runs must be int32 and sink int32 [num_workers]")
+    desc = cache_desc(k_pool)
+    _check(lib().pkv_measure_gather(_ptr(k_pool), _ptr(v_pool), ctypes.byref(desc), _ptr(runs),
+                                    runs.numel(), int(num_workers), int(runs_in_flight),
+                                    _ptr(sink), _stream(stream)))
 
 
 # --------------------------------------------------------- host checks

@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
 
-HIP_SOURCES = ["cache_ops.hip", "decode.hip", "prefill.hip"]
+HIP_SOURCES = ["cache_ops.hip", "decode.hip", "prefill.hip", "measure.hip"]
 C_SOURCES = ["alloc.c"]
 
 ARCH = "gfx950"
