@@ -393,6 +393,42 @@ int pkv_alloc_export(const pkv_alloc* a, int32_t* free_fifo_out, int32_t* num_fr
                      int32_t* ref_cnt_out);
 
 /*
+ * Checkpoint and restore of the whole allocator state: free-list order,
+ * reference counts, every live sequence (id, length, block table, and the
+ * token ids and chain hash it enters prefix-cache blocks with), the prefix
+ * cache (entries and hit/query/eviction counters) and the host pool (free
+ * list and counts).  A handle restored from a saved state answers every later
+ * call as the saved one would.  The state is a flat array of int64 words,
+ * little-endian as the host writes them:
+ *   magic "PKVSTATE", version 1, num_blocks, block_size, prefix caching on,
+ *   host blocks, free blocks F, live sequences S, cached blocks C, hits,
+ *   queries, evictions, free host blocks FH;
+ *   the free list head to tail (F words); the reference counts (num_blocks);
+ *   per sequence, ids ascending: id, length, block count n, flags (1: token
+ *   ids tracked, 2: swapped out), chain hash, the n table entries, then
+ *   block_size token ids when tracked;
+ *   per cached block, ids ascending: block, key, parent key, its block_size
+ *   token ids; the host free list head to tail (FH); the host counts.
+ *
+ * pkv_alloc_save_bytes: bytes the current state needs (0 and an error on a
+ *   NULL handle).
+ * pkv_alloc_save: writes the state to buf (host, >= that many bytes) and the
+ *   byte count to *written (may be NULL).  Errors: PKV_EINVAL.
+ * pkv_alloc_restore: a new handle (owned by the caller, released with
+ *   pkv_alloc_destroy) holding a saved state; NULL with pkv_last_error() set
+ *   when the words are not a consistent state (bad magic or sizes, ids out of
+ *   range, counts that disagree with the tables and free lists, trailing
+ *   words).
+ * pkv_alloc_seq_ids: the live sequence ids, ascending, into ids_out (host,
+ *   max_ids entries); *num_out receives their count.  Errors: PKV_EINVAL
+ *   (including max_ids below the count).
+ */
+size_t pkv_alloc_save_bytes(const pkv_alloc* a);
+int pkv_alloc_save(const pkv_alloc* a, void* buf, size_t bytes, size_t* written);
+pkv_alloc* pkv_alloc_restore(const void* buf, size_t bytes);
+int pkv_alloc_seq_ids(const pkv_alloc* a, int64_t* ids_out, int32_t max_ids, int32_t* num_out);
+
+/*
  * Prefix caching (weishuz.com Month 2, section 04: a computed prompt's K/V
  * stay in device memory and a later prompt with the same leading tokens maps
  * the same blocks instead of computing them again; section 03 reading (2): a

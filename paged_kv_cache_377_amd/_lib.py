@@ -86,6 +86,10 @@ _SIGS = {
     "pkv_build_tables": (_i32, [_vp, _vp, _i32, _vp, _i32, _vp]),
     "pkv_alloc_stats": (_i32, [_vp, _P(Stats)]),
     "pkv_alloc_export": (_i32, [_vp, _vp, _vp, _vp]),
+    "pkv_alloc_save_bytes": (_sz, [_vp]),
+    "pkv_alloc_save": (_i32, [_vp, _vp, _sz, _vp]),
+    "pkv_alloc_restore": (_vp, [_vp, _sz]),
+    "pkv_alloc_seq_ids": (_i32, [_vp, _vp, _i32, _vp]),
     "pkv_prefix_cache_enable": (_i32, [_vp]),
     "pkv_seq_add_tokens": (_i32, [_vp, _i64, _vp, _i32, _vp, _vp]),
     "pkv_seq_append_token": (_i32, [_vp, _i64, _i32, _vp, _vp]),
@@ -462,6 +466,39 @@ class BlockAllocator:
         self._h = h
         if prefix_caching:
             _check(self._l.pkv_prefix_cache_enable(h))
+
+    @classmethod
+    def restore(cls, state: bytes) -> "BlockAllocator":
+        """A new allocator holding a state written by save()."""
+        l = lib()
+        buf = ctypes.create_string_buffer(bytes(state), len(state))
+        h = l.pkv_alloc_restore(buf, len(state))
+        if not h:
+            raise PagedKVError(PKV_EINVAL, l.pkv_last_error().decode())
+        obj = cls.__new__(cls)
+        obj._l = l
+        obj._h = h
+        words = np.frombuffer(bytes(state[: 8 * 6]), dtype="<i8")
+        obj.num_blocks, obj.block_size = int(words[2]), int(words[3])
+        if int(words[5]):
+            obj.num_host_blocks = int(words[5])
+        return obj
+
+    def save(self) -> bytes:
+        """The whole allocator state (see pkv_alloc_save in include/pagedkv.h)."""
+        n = int(self._l.pkv_alloc_save_bytes(self._h))
+        buf = ctypes.create_string_buffer(max(n, 8))
+        written = ctypes.c_size_t()
+        _check(self._l.pkv_alloc_save(self._h, buf, n, ctypes.byref(written)))
+        return buf.raw[: written.value]
+
+    def seq_ids(self) -> List[int]:
+        """Live sequence ids, ascending."""
+        n = self.stats()["num_seqs"]
+        out = np.empty(max(n, 1), dtype=np.int64)
+        k = ctypes.c_int32()
+        _check(self._l.pkv_alloc_seq_ids(self._h, out.ctypes.data, n, ctypes.byref(k)))
+        return out[: k.value].tolist()
 
     def close(self):
         if getattr(self, "_h", None):

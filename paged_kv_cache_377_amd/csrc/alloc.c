@@ -995,6 +995,322 @@ int pkv_alloc_export(const pkv_alloc* a, int32_t* free_fifo_out, int32_t* num_fr
   return PKV_OK;
 }
 
+/* ------------------------------------------------------ save / restore */
+/*
+ * The whole allocator state as a flat array of int64 words (uint64 hashes
+ * stored as their bit patterns):
+ *   [0] magic  [1] version  [2] num_blocks  [3] block_size  [4] prefix on
+ *   [5] host blocks  [6] free blocks  [7] live sequences  [8] cached blocks
+ *   [9] hits  [10] queries  [11] evictions  [12] free host blocks
+ *   free list, head to tail                         (free blocks words)
+ *   reference counts                                (num_blocks words)
+ *   per live sequence, ids ascending: id, length, blocks, flags (1 tracked,
+ *     2 swapped), chain hash, the block table, then block_size token ids
+ *     when tracked (the partial last block's ids first)
+ *   per cached block, ids ascending: block, key, parent key, its token ids
+ *   free host list, head to tail; host reference counts
+ * Scratch (step stamps, marks) is not state: a restored handle behaves as
+ * the saved one on every later call.
+ */
+enum { kSaveHeader = 13 };
+static const int64_t kSaveMagic = 0x4554415453564B50LL; /* "PKVSTATE" */
+static const int64_t kSaveVersion = 1;
+
+static int cmp_i64(const void* x, const void* y) {
+  const int64_t a = *(const int64_t*)x, b = *(const int64_t*)y;
+  return (a > b) - (a < b);
+}
+
+static size_t save_words(const pkv_alloc* a) {
+  size_t w = kSaveHeader + (size_t)a->nfree + (size_t)a->num_blocks;
+  for (size_t i = 0; i < a->tcap; ++i) {
+    const seq_entry* e = &a->tab[i];
+    if (e->state != 1) continue;
+    w += 5 + (size_t)e->nblk + (e->tracked ? (size_t)a->block_size : 0);
+  }
+  if (a->prefix) w += (size_t)a->ncached * (3 + (size_t)a->block_size);
+  w += (size_t)a->hnfree + (size_t)a->hnum;
+  return w;
+}
+
+size_t pkv_alloc_save_bytes(const pkv_alloc* a) {
+  pkv__clear_error();
+  if (!a) {
+    pkv__fail(PKV_EINVAL, "allocator handle is NULL");
+    return 0;
+  }
+  return save_words(a) * sizeof(int64_t);
+}
+
+int pkv_alloc_seq_ids(const pkv_alloc* a, int64_t* ids_out, int32_t max_ids, int32_t* num_out) {
+  pkv__clear_error();
+  if (!a || !num_out || max_ids < 0 || (max_ids > 0 && !ids_out))
+    return pkv__fail(PKV_EINVAL, "bad argument");
+  if ((size_t)max_ids < a->nlive)
+    return pkv__fail(PKV_EINVAL, "%zu live sequences, room for %d", a->nlive, max_ids);
+  int32_t k = 0;
+  for (size_t i = 0; i < a->tcap; ++i)
+    if (a->tab[i].state == 1) ids_out[k++] = a->tab[i].id;
+  qsort(ids_out, (size_t)k, sizeof(int64_t), cmp_i64);
+  *num_out = k;
+  return PKV_OK;
+}
+
+int pkv_alloc_save(const pkv_alloc* a, void* buf, size_t bytes, size_t* written) {
+  pkv__clear_error();
+  if (!a || (!buf && bytes)) return pkv__fail(PKV_EINVAL, "bad argument");
+  const size_t need = save_words(a);
+  if (bytes < need * sizeof(int64_t))
+    return pkv__fail(PKV_EINVAL, "buffer of %zu bytes, the state needs %zu", bytes,
+                     need * sizeof(int64_t));
+  int64_t* ids = (int64_t*)malloc((a->nlive ? a->nlive : 1) * sizeof(int64_t));
+  if (!ids) return pkv__fail(PKV_EINVAL, "out of host memory");
+  int32_t nseq = 0;
+  pkv_alloc_seq_ids(a, ids, (int32_t)a->nlive, &nseq);
+  int64_t* w = (int64_t*)buf;
+  const int32_t B = a->block_size;
+  size_t k = 0;
+  w[k++] = kSaveMagic;
+  w[k++] = kSaveVersion;
+  w[k++] = a->num_blocks;
+  w[k++] = B;
+  w[k++] = a->prefix;
+  w[k++] = a->hnum;
+  w[k++] = a->nfree;
+  w[k++] = nseq;
+  w[k++] = a->prefix ? a->ncached : 0;
+  w[k++] = a->hits;
+  w[k++] = a->queries;
+  w[k++] = a->evictions;
+  w[k++] = a->hnfree;
+  for (int32_t b = a->fhead; b >= 0; b = a->nxt[b]) w[k++] = b;
+  for (int32_t b = 0; b < a->num_blocks; ++b) w[k++] = a->ref[b];
+  for (int32_t i = 0; i < nseq; ++i) {
+    const seq_entry* e = find(a, ids[i]);
+    w[k++] = e->id;
+    w[k++] = e->len;
+    w[k++] = e->nblk;
+    w[k++] = (e->tracked ? 1 : 0) | (e->swapped ? 2 : 0);
+    w[k++] = e->tracked ? (int64_t)e->chain : 0; /* unused once ids are unknown */
+    for (int32_t j = 0; j < e->nblk; ++j) w[k++] = e->blocks[j];
+    if (e->tracked)
+      for (int32_t j = 0; j < B; ++j) w[k++] = e->toks[j];
+  }
+  free(ids);
+  if (a->prefix)
+    for (int32_t b = 0; b < a->num_blocks; ++b) {
+      if (!a->bcached[b]) continue;
+      w[k++] = b;
+      w[k++] = (int64_t)a->bkey[b];
+      w[k++] = (int64_t)a->bpar[b];
+      for (int32_t j = 0; j < B; ++j) w[k++] = a->btok[(size_t)b * B + j];
+    }
+  for (int32_t i = 0; i < a->hnfree; ++i) {
+    int64_t j = (int64_t)a->hhead + i;
+    if (j >= a->hnum) j -= a->hnum;
+    w[k++] = a->hfifo[j];
+  }
+  for (int32_t h = 0; h < a->hnum; ++h) w[k++] = a->href[h];
+  if (written) *written = k * sizeof(int64_t);
+  return PKV_OK;
+}
+
+/* restore: reading words with bounds and range checks */
+typedef struct {
+  const int64_t* w;
+  size_t n, k;
+  int bad;
+} reader;
+
+static int64_t rd(reader* r, int64_t lo, int64_t hi) {
+  if (r->bad || r->k >= r->n) {
+    r->bad = 1;
+    return lo;
+  }
+  const int64_t x = r->w[r->k++];
+  if (x < lo || x > hi) {
+    r->bad = 1;
+    return lo;
+  }
+  return x;
+}
+
+pkv_alloc* pkv_alloc_restore(const void* buf, size_t bytes) {
+  pkv__clear_error();
+  if (!buf || bytes % sizeof(int64_t) || bytes < kSaveHeader * sizeof(int64_t)) {
+    pkv__fail(PKV_EINVAL, "saved state of %zu bytes is not a whole state", bytes);
+    return NULL;
+  }
+  reader r = {(const int64_t*)buf, bytes / sizeof(int64_t), 0, 0};
+  if (rd(&r, kSaveMagic, kSaveMagic) != kSaveMagic || r.bad ||
+      rd(&r, kSaveVersion, kSaveVersion) != kSaveVersion || r.bad) {
+    pkv__fail(PKV_EINVAL, "not a saved allocator state (magic or version)");
+    return NULL;
+  }
+  const int32_t N = (int32_t)rd(&r, 1, INT32_MAX);
+  const int32_t B = (int32_t)rd(&r, 1, INT32_MAX);
+  const int prefix = (int)rd(&r, 0, 1);
+  const int32_t H = (int32_t)rd(&r, 0, INT32_MAX);
+  const int32_t nfree = (int32_t)rd(&r, 0, N);
+  const int64_t nseq = rd(&r, 0, INT32_MAX);
+  const int32_t ncached = (int32_t)rd(&r, 0, N);
+  const int64_t hits = rd(&r, 0, INT64_MAX);
+  const int64_t queries = rd(&r, 0, INT64_MAX);
+  const int64_t evictions = rd(&r, 0, INT64_MAX);
+  const int32_t hnfree = (int32_t)rd(&r, 0, H);
+  if (r.bad || (!prefix && ncached)) {
+    pkv__fail(PKV_EINVAL, "saved state has a bad header");
+    return NULL;
+  }
+  pkv_alloc* a = pkv_alloc_create(N, B, NULL);
+  if (!a) return NULL;
+  int32_t* count = (int32_t*)calloc((size_t)N, sizeof(int32_t));
+  int32_t* hcount = (int32_t*)calloc(H ? (size_t)H : 1, sizeof(int32_t));
+  const char* why = NULL;
+  if (!count || !hcount) {
+    why = "out of host memory";
+    goto fail;
+  }
+  if (prefix && pkv_prefix_cache_enable(a) != PKV_OK) {
+    why = "out of host memory";
+    goto fail;
+  }
+  if (H && pkv_alloc_set_host_pool(a, H, NULL) != PKV_OK) {
+    why = "out of host memory";
+    goto fail;
+  }
+  /* free list: relink in the saved order */
+  a->fhead = a->ftail = -1;
+  a->nfree = 0;
+  for (int32_t i = 0; i < N; ++i) a->nxt[i] = a->prv[i] = -1;
+  for (int32_t i = 0; i < nfree; ++i) {
+    const int32_t b = (int32_t)rd(&r, 0, N - 1);
+    if (r.bad || count[b]) {
+      why = "free list: block out of range or listed twice";
+      goto fail;
+    }
+    count[b] = 1;
+    return_block(a, b);
+  }
+  memset(count, 0, (size_t)N * sizeof(int32_t));
+  for (int32_t b = 0; b < N; ++b) a->ref[b] = (int32_t)rd(&r, 0, INT32_MAX);
+  if (r.bad) {
+    why = "bad reference count";
+    goto fail;
+  }
+  int64_t prev_id = 0;
+  for (int64_t i = 0; i < nseq; ++i) {
+    const int64_t id = rd(&r, INT64_MIN, INT64_MAX);
+    const int32_t len = (int32_t)rd(&r, 0, INT32_MAX);
+    const int32_t nblk = (int32_t)rd(&r, 0, INT32_MAX);
+    const int flags = (int)rd(&r, 0, 3);
+    const uint64_t chain = (uint64_t)rd(&r, INT64_MIN, INT64_MAX);
+    if (r.bad || (i > 0 && id <= prev_id) || nblk != (int32_t)(((int64_t)len + B - 1) / B) ||
+        ((flags & 1) && !prefix) || ((flags & 2) && !H)) {
+      why = "bad sequence record (order, length, block count or flags)";
+      goto fail;
+    }
+    prev_id = id;
+    seq_entry* e = insert(a, id);
+    if (!e || reserve_blocks(e, nblk) != PKV_OK) {
+      why = "out of host memory";
+      goto fail;
+    }
+    e->len = len;
+    e->nblk = nblk;
+    e->swapped = (flags & 2) ? 1 : 0;
+    const int32_t lim = e->swapped ? H : N;
+    for (int32_t j = 0; j < nblk; ++j) {
+      const int32_t b = (int32_t)rd(&r, 0, lim - 1);
+      if (r.bad) {
+        why = "block table entry out of range";
+        goto fail;
+      }
+      e->blocks[j] = b;
+      if (e->swapped) hcount[b]++; else count[b]++;
+    }
+    if (flags & 1) {
+      e->toks = (int32_t*)malloc((size_t)B * sizeof(int32_t));
+      if (!e->toks) {
+        why = "out of host memory";
+        goto fail;
+      }
+      for (int32_t j = 0; j < B; ++j) e->toks[j] = (int32_t)rd(&r, INT32_MIN, INT32_MAX);
+      e->tracked = 1;
+      e->chain = chain;
+    }
+  }
+  for (int32_t b = 0; b < N; ++b)
+    if (a->ref[b] != count[b] || (a->ref[b] == 0) != (a->prv[b] >= 0 || a->fhead == b)) {
+      why = "reference counts disagree with the block tables or the free list";
+      goto fail;
+    }
+  if (a->nfree != nfree) {
+    why = "free list length";
+    goto fail;
+  }
+  for (int32_t i = 0; i < ncached; ++i) {
+    const int32_t b = (int32_t)rd(&r, 0, N - 1);
+    const uint64_t key = (uint64_t)rd(&r, INT64_MIN, INT64_MAX);
+    const uint64_t par = (uint64_t)rd(&r, INT64_MIN, INT64_MAX);
+    if (r.bad || a->bcached[b]) {
+      why = "cached block out of range or listed twice";
+      goto fail;
+    }
+    for (int32_t j = 0; j < B; ++j)
+      a->btok[(size_t)b * B + j] = (int32_t)rd(&r, INT32_MIN, INT32_MAX);
+    int found;
+    const size_t slot = map_probe(a, key, par, a->btok + (size_t)b * B, &found);
+    if (r.bad || found) {
+      why = "cached block entry repeated";
+      goto fail;
+    }
+    a->map[slot] = b;
+    a->bkey[b] = key;
+    a->bpar[b] = par;
+    a->bcached[b] = 1;
+    a->ncached++;
+  }
+  a->hits = hits;
+  a->queries = queries;
+  a->evictions = evictions;
+  if (H) {
+    memset(a->hmark, 0, (size_t)H * sizeof(int32_t));
+    for (int32_t i = 0; i < hnfree; ++i) {
+      const int32_t h = (int32_t)rd(&r, 0, H - 1);
+      if (r.bad || a->hmark[h]) {
+        why = "host free list: block out of range or listed twice";
+        goto fail;
+      }
+      a->hmark[h] = 1;
+      a->hfifo[i] = h;
+    }
+    a->hhead = 0;
+    a->hnfree = hnfree;
+    for (int32_t h = 0; h < H; ++h) {
+      a->href[h] = (int32_t)rd(&r, 0, INT32_MAX);
+      if (r.bad || a->href[h] != hcount[h] || (a->href[h] == 0) != (a->hmark[h] == 1)) {
+        why = "host reference counts disagree with the tables or the host free list";
+        goto fail;
+      }
+    }
+    memset(a->hmark, 0, (size_t)H * sizeof(int32_t));
+  }
+  if (r.k != r.n) {
+    why = "trailing words after the saved state";
+    goto fail;
+  }
+  free(count);
+  free(hcount);
+  return a;
+fail:
+  free(count);
+  free(hcount);
+  pkv_alloc_destroy(a);
+  pkv__fail(PKV_EINVAL, "saved allocator state rejected: %s", why ? why : "truncated");
+  return NULL;
+}
+
 /* ------------------------------------------------------ contract checks */
 
 int pkv_validate_write(const int64_t* slot_mapping, int32_t num_tokens, const pkv_cache_desc* c) {

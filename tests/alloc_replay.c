@@ -3,7 +3,9 @@
  * Input lines:  N B perm...  then  add s n | fork p c | append s |
  *               step k s1..sk | free s | table s | prefix |
  *               addt s k t1..tk | appt s t | stept k s1..sk t1..tk |
- *               look k t1..tk | hpool n | sout k s1..sk | sin k s1..sk
+ *               look k t1..tk | hpool n | sout k s1..sk | sin k s1..sk |
+ *               saveload (save the state, destroy the handle, go on with
+ *               a handle restored from the saved words)
  * Output: one line per op with the return code and results. */
 #include <stdio.h>
 #include <stdlib.h>
@@ -22,7 +24,19 @@ int main(void) {
   if (!a) return 3;
   char op[16];
   while (scanf("%15s", op) == 1) {
-    if (strcmp(op, "hpool") == 0) {
+    if (strcmp(op, "saveload") == 0) {
+      size_t nb = pkv_alloc_save_bytes(a), wr = 0;
+      void* buf = malloc(nb ? nb : 8);
+      int rc = pkv_alloc_save(a, buf, nb, &wr);
+      if (rc == 0) {
+        pkv_alloc* r = pkv_alloc_restore(buf, wr);
+        if (!r) { printf("saveload restore failed: %s\n", pkv_last_error()); return 4; }
+        pkv_alloc_destroy(a);
+        a = r;
+      }
+      free(buf);
+      printf("saveload %d\n", rc);
+    } else if (strcmp(op, "hpool") == 0) {
       int hn;
       if (scanf("%d", &hn) != 1) return 2;
       printf("hpool %d\n", pkv_alloc_set_host_pool(a, hn, NULL));

@@ -88,13 +88,31 @@ def _random_stream(seed, steps=300):
     return rnd, B, N, order, ids
 
 
+def roundtrip(c):
+    """Save the allocator, restore the state into a fresh handle, check that
+    the new handle saves the same words, and hand it back (the old one is
+    closed: every later call goes to the restored state)."""
+    state = c.save()
+    r = pkv.BlockAllocator.restore(state)
+    assert r.save() == state
+    assert r.export() == c.export()
+    assert r.seq_ids() == c.seq_ids()
+    c.close()
+    return r
+
+
 @pytest.mark.parametrize("seed", range(40))
 def test_random_streams_match_oracle(seed):
+    """Odd seeds also save and restore the allocator every 37 ops and continue
+    the stream on the restored handle."""
     rnd, B, N, order, ids = _random_stream(seed)
     c = pkv.BlockAllocator(N, B, order)
     o = BlockAllocatorModel(N, B, order)
     w = ContentWorld(N, B)
-    for _ in range(300):
+    for step_no in range(300):
+        if seed % 2 and step_no % 37 == 36:
+            c = roundtrip(c)
+            assert c.seq_ids() == sorted(o.seqs)
         live = list(o.seqs)
         r = rnd.random()
         if r < 0.15:
@@ -179,6 +197,8 @@ def _replay_lines(seed):
             lines.append(f"step {k} " + " ".join(map(str, batch)))
         elif r < 0.9:
             lines.append(f"free {s}")
+        elif r < 0.95:
+            lines.append("saveload")
         else:
             lines.append(f"table {s}")
     return lines, B, N, order
@@ -212,6 +232,8 @@ def _oracle_replay(lines, B, N, order, model=None):
                 if s not in o.seqs:
                     raise AllocError(-1, "unknown")
                 out.append(f"table 0 {o.length(s)} :" + "".join(f" {b}" for b in o.table(s)))
+            elif f[0] == "saveload":  # the C side continues on a restored handle
+                out.append("saveload 0")
         except AllocError as e:
             out.append(f"{f[0]} {e.code}")
     out.append("final free" + "".join(f" {b}" for b in o.free_list()) + " | ref" +
@@ -268,6 +290,8 @@ def _prefix_replay_lines(seed):
             lines.append(f"free {s}")
         elif r < 0.92:
             lines.append(f"look {len(toks)} " + " ".join(map(str, toks)))
+        elif r < 0.96:
+            lines.append("saveload")
         else:
             lines.append(f"table {s}")
     return lines, B, N, order
@@ -344,6 +368,8 @@ def _swap_replay_lines(seed):
             lines.append(f"sin {k} " + " ".join(str(rnd.choice(ids)) for _ in range(k)))
         elif r < 0.9:
             lines.append(f"free {s}")
+        elif r < 0.95:
+            lines.append("saveload")
         else:
             lines.append(f"table {s}")
     return lines, B, N, order, H
@@ -392,3 +418,44 @@ def test_sanitizer_replay_matches_oracle(replay_bin, seed):
     assert r.returncode == 0, r.stderr[-2000:]
     assert "ERROR: AddressSanitizer" not in r.stderr and "runtime error" not in r.stderr
     assert r.stdout.strip().splitlines() == _oracle_replay(lines, B, N, order)
+
+
+def test_restore_rejects_states_that_do_not_add_up():
+    """A restored state must be whole and consistent: truncated or padded
+    words, another magic, a reference count that disagrees with the tables, a
+    block listed twice in the free list all fail with PKV_EINVAL."""
+    c = pkv.BlockAllocator(12, 4, list(range(11, -1, -1)), prefix_caching=True)
+    c.set_host_pool(6)
+    c.add_tokens(3, [1, 2, 3, 4, 5, 6])
+    c.fork(3, 4)
+    c.step([3, 4], [7, 8])
+    c.add(-9, 5)
+    c.swap_out([-9])
+    good = c.save()
+    pkv.BlockAllocator.restore(good).close()
+    w = np.frombuffer(good, dtype="<i8").copy()
+    nfree = int(w[6])
+    bad = {
+        "truncated": good[:-8],
+        "trailing": good + bytes(8),
+        "odd length": good[:-3],
+        "magic": b"X" + good[1:],
+    }
+    v = w.copy(); v[13 + nfree] += 1                         # block 0's count off by one
+    bad["ref count"] = v.tobytes()
+    v = w.copy(); v[14] = v[13]                              # a block twice in the free list
+    bad["free twice"] = v.tobytes()
+    v = w.copy(); v[2] = 0                                   # no blocks
+    bad["num_blocks"] = v.tobytes()
+    for name, data in bad.items():
+        with pytest.raises(pkv.PagedKVError) as e:
+            pkv.BlockAllocator.restore(data)
+        assert e.value.code == pkv.PKV_EINVAL, name
+
+
+def test_seq_ids_lists_live_sequences():
+    c = pkv.BlockAllocator(8, 2)
+    for s in (5, -3, 2 ** 40, 0):
+        c.add(s, 1)
+    c.free(0)
+    assert c.seq_ids() == [-3, 5, 2 ** 40]

@@ -8,6 +8,7 @@ import pytest
 
 import paged_kv_cache_377_amd as pkv
 from oracle import BlockAllocatorModel
+from tests.test_alloc_c import roundtrip
 from tests.test_alloc_c import _both, _same_state
 
 
@@ -67,7 +68,9 @@ def test_random_streams_match_oracle(seed):
     c.set_host_pool(H, horder)
     o.set_host_pool(H, horder)
     nid = 0
-    for _ in range(300):
+    for step_no in range(300):
+        if seed % 2 and step_no % 29 == 28:  # continue on a restored handle
+            c = roundtrip(c)
         live, out = sorted(o.seqs), sorted(o.swapped)
         r = rng.random()
         if r < 0.2 or not (live or out):
