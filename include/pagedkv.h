@@ -30,6 +30,13 @@
  *     block_size in {8, 16, 32}, query heads per KV head in {1, 2, 4, 8}.
  *     Other shapes return PKV_EUNSUPPORTED.
  *   - The allocator is not thread-safe: one scheduler thread owns a handle.
+ *   - Debugging: with PKV_VALIDATE set to anything but "0" in the environment
+ *     (read on every call), each device call first copies its index arrays
+ *     (slots, copy pairs, tables, lengths, row starts) to the host,
+ *     synchronously on its stream, and checks them by the rules of the
+ *     pkv_validate_* calls below; a violation returns PKV_ERANGE and nothing
+ *     is launched.  This waits for the stream: not for timing or graph
+ *     capture.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H

@@ -61,6 +61,11 @@ void pkv__clear_error(void) { g_err[0] = '\0'; }
 
 const char* pkv_last_error(void) { return g_err; }
 
+int pkv__validate_enabled(void) {
+  const char* v = getenv("PKV_VALIDATE");
+  return v && v[0] && strcmp(v, "0") != 0;
+}
+
 int pkv__check_desc(const pkv_cache_desc* c) {
   if (!c) return pkv__fail(PKV_EINVAL, "cache descriptor is NULL");
   if (c->num_blocks <= 0 || c->num_kv_heads <= 0 || c->block_size <= 0 || c->head_dim <= 0)

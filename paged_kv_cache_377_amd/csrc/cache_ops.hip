@@ -14,6 +14,8 @@
 //    block src's contents.
 #include <hip/hip_runtime.h>
 
+#include <stdlib.h>
+
 #include <stdint.h>
 
 #include "pkv_internal.h"
@@ -99,6 +101,51 @@ int elem_bytes(int32_t dtype) { return dtype == PKV_BF16 ? 2 : 4; }
 
 }  // namespace
 
+extern "C" int pkv__copy_to_host(void* dst, const void* src, size_t bytes, void* stream) {
+  hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDefault, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return pkv__fail(PKV_EHIP, "validation copy: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+namespace {
+
+// PKV_VALIDATE checks of the index arrays of a write, a copy and a swap.
+int validate_write_device(const int64_t* slots, int32_t n, const pkv_cache_desc* c, void* stream) {
+  int64_t* h = (int64_t*)malloc((size_t)n * sizeof(int64_t));
+  if (!h) return pkv__fail(PKV_EINVAL, "out of host memory");
+  int rc = pkv__copy_to_host(h, slots, (size_t)n * sizeof(int64_t), stream);
+  if (!rc) rc = pkv_validate_write(h, n, c);
+  free(h);
+  return rc;
+}
+
+int validate_pairs_device(const int32_t* pairs, int32_t n, int32_t src_blocks, int32_t dst_blocks,
+                          const pkv_cache_desc* c, bool same_pool, void* stream) {
+  int32_t* h = (int32_t*)malloc((size_t)n * 2 * sizeof(int32_t));
+  if (!h) return pkv__fail(PKV_EINVAL, "out of host memory");
+  int rc = pkv__copy_to_host(h, pairs, (size_t)n * 2 * sizeof(int32_t), stream);
+  if (!rc && same_pool) rc = pkv_validate_copy(h, n, c);
+  if (!rc && !same_pool) {
+    // two pools: ids in their own pool, destinations distinct
+    uint8_t* seen = (uint8_t*)calloc((size_t)dst_blocks, 1);
+    if (!seen) rc = pkv__fail(PKV_EINVAL, "out of host memory");
+    for (int32_t i = 0; !rc && i < n; ++i) {
+      const int32_t s = h[2 * i], d = h[2 * i + 1];
+      if (s < 0 || s >= src_blocks || d < 0 || d >= dst_blocks)
+        rc = pkv__fail(PKV_ERANGE, "pair %d = (%d, %d) outside the pools (%d, %d blocks)", i, s, d,
+                       src_blocks, dst_blocks);
+      else if (seen[d]++)
+        rc = pkv__fail(PKV_ERANGE, "pair %d: destination block %d appears twice", i, d);
+    }
+    free(seen);
+  }
+  free(h);
+  return rc;
+}
+
+}  // namespace
+
 extern "C" int pkv_paged_kv_write(const void* k, const void* v, const int64_t* slot_mapping,
                                   int32_t num_tokens, void* k_cache, void* v_cache,
                                   const pkv_cache_desc* c, void* stream) {
@@ -121,6 +168,10 @@ extern "C" int pkv_paged_kv_write(const void* k, const void* v, const int64_t* s
   if (total > INT32_MAX)
     return pkv__fail(PKV_EINVAL, "write of %lld 16-byte pieces is too large (limit 2^31 - 1)",
                      (long long)total);
+  if (pkv__validate_enabled()) {
+    rc = validate_write_device(slot_mapping, num_tokens, c, stream);
+    if (rc) return rc;
+  }
   const int64_t grid = (total + kThreads - 1) / kThreads;
   hipLaunchKernelGGL(kv_write_kernel, dim3((uint32_t)grid), dim3(kThreads), 0,
                      (hipStream_t)stream, (const uint4*)k, (const uint4*)v, slot_mapping,
@@ -151,6 +202,11 @@ extern "C" int pkv_copy_blocks(void* k_cache, void* v_cache, const pkv_cache_des
   const int32_t groups = (block_chunks + kThreads - 1) / kThreads;
   const int64_t grid = (int64_t)num_pairs * groups;
   if (grid > INT32_MAX) return pkv__fail(PKV_EINVAL, "copy too large");
+  if (pkv__validate_enabled()) {
+    rc = validate_pairs_device(src_dst_pairs, num_pairs, c->num_blocks, c->num_blocks, c, true,
+                               stream);
+    if (rc) return rc;
+  }
   hipLaunchKernelGGL(copy_blocks_kernel, dim3((uint32_t)grid), dim3(kThreads), 0,
                      (hipStream_t)stream, (uint4*)k_cache, (uint4*)v_cache, src_dst_pairs,
                      block_chunks, groups, c->num_blocks);
@@ -185,6 +241,11 @@ extern "C" int pkv_swap_blocks(void* dst_k, void* dst_v, int32_t dst_num_blocks,
   const int32_t groups = (block_chunks + kThreads - 1) / kThreads;
   const int64_t grid = (int64_t)num_pairs * groups;
   if (grid > INT32_MAX) return pkv__fail(PKV_EINVAL, "swap too large");
+  if (pkv__validate_enabled()) {
+    const int rc = validate_pairs_device(pairs, num_pairs, src_num_blocks, dst_num_blocks, c,
+                                         false, stream);
+    if (rc) return rc;
+  }
   hipLaunchKernelGGL(swap_blocks_kernel, dim3((uint32_t)grid), dim3(kThreads), 0,
                      (hipStream_t)stream, (uint4*)dst_k, (uint4*)dst_v, dst_num_blocks,
                      (const uint4*)src_k, (const uint4*)src_v, src_num_blocks, pairs, block_chunks,

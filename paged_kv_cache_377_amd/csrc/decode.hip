@@ -43,6 +43,7 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+#include <stdlib.h>
 #include <stdint.h>
 
 #include <algorithm>
@@ -1386,6 +1387,21 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
                      workspace_bytes, pl.bytes);
   if (pl.bytes && !aligned16(workspace))
     return pkv__fail(PKV_EINVAL, "workspace must be 16-byte aligned");
+
+  if (pkv__validate_enabled()) {
+    // debug: the contract of tables and lengths, checked on the host first
+    const size_t nt = (size_t)num_seqs * max_blocks_per_seq;
+    int32_t* ht = (int32_t*)malloc((nt ? nt : 1) * sizeof(int32_t));
+    int32_t* hc = (int32_t*)malloc((size_t)num_seqs * sizeof(int32_t));
+    rc = (ht && hc) ? PKV_OK : pkv__fail(PKV_EINVAL, "out of host memory");
+    if (!rc && nt) rc = pkv__copy_to_host(ht, block_tables, nt * sizeof(int32_t), stream);
+    if (!rc) rc = pkv__copy_to_host(hc, context_lens, (size_t)num_seqs * sizeof(int32_t), stream);
+    if (!rc)
+      rc = pkv_validate_decode(ht, max_blocks_per_seq, hc, num_seqs, max_context_len, c);
+    free(ht);
+    free(hc);
+    if (rc) return rc;
+  }
 
   LaunchArgs a;
   a.out = out;

@@ -21,6 +21,16 @@ void pkv__clear_error(void);
 /* Basic checks of a cache descriptor shared by every device call. */
 int pkv__check_desc(const pkv_cache_desc* c);
 
+/* Non-zero when the environment sets PKV_VALIDATE to a value other than "0"
+ * (read on every call): the device calls then copy their index arrays to the
+ * host, synchronously, and check them before launching anything. */
+int pkv__validate_enabled(void);
+
+/* Copy `bytes` from device (or pinned host) memory to host memory after the
+ * work already queued on `stream` (a hipStream_t), synchronously; used by the
+ * PKV_VALIDATE checks only.  PKV_EHIP on error. */
+int pkv__copy_to_host(void* dst, const void* src, size_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

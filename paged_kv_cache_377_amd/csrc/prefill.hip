@@ -41,6 +41,7 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+#include <stdlib.h>
 
 #include <type_traits>
 
@@ -648,6 +649,25 @@ extern "C" int pkv_paged_attention_prefill(
   const int64_t tps = (max_new_tokens + tokens_per_group - 1) / tokens_per_group;
   const int64_t grid = tps * num_seqs * c->num_kv_heads;
   if (grid > INT32_MAX) return pkv__fail(PKV_EINVAL, "prefill grid too large");
+  if (pkv__validate_enabled()) {
+    // debug: the contract of tables, lengths and row ranges, checked on the host first
+    const size_t nt = (size_t)num_seqs * max_blocks_per_seq;
+    int32_t* ht = (int32_t*)malloc((nt ? nt : 1) * sizeof(int32_t));
+    int32_t* hc = (int32_t*)malloc((size_t)num_seqs * sizeof(int32_t));
+    int32_t* hq = (int32_t*)malloc((size_t)(num_seqs + 1) * sizeof(int32_t));
+    rc = (ht && hc && hq) ? PKV_OK : pkv__fail(PKV_EINVAL, "out of host memory");
+    if (!rc && nt) rc = pkv__copy_to_host(ht, block_tables, nt * sizeof(int32_t), stream);
+    if (!rc) rc = pkv__copy_to_host(hc, context_lens, (size_t)num_seqs * sizeof(int32_t), stream);
+    if (!rc)
+      rc = pkv__copy_to_host(hq, query_start_loc, (size_t)(num_seqs + 1) * sizeof(int32_t), stream);
+    if (!rc)
+      rc = pkv_validate_prefill(ht, max_blocks_per_seq, hc, hq, num_seqs, num_tokens,
+                                max_new_tokens, max_context_len, c);
+    free(ht);
+    free(hc);
+    free(hq);
+    if (rc) return rc;
+  }
   const int log2b = B == 8 ? 3 : (B == 16 ? 4 : 5);
   const float qscale = scale * 1.4426950408889634f;  // logits in log2 units
   hipStream_t st = (hipStream_t)stream;
