@@ -187,16 +187,27 @@ def test_empty_launches_do_nothing():
     torch.cuda.synchronize()
 
 
-def test_values_beyond_fp16_take_the_bf16_path():
-    """V entries far past fp16's range (bf16 holds them) still match the
-    oracle: V enters the P V product in bf16, whatever its magnitude."""
+@pytest.mark.parametrize("values", [
+    (3.0e5, -1.2e6, 7.0e4),      # past fp16's largest finite value
+    (3.0e4, -6.0e4, 1.5e4),      # large, in rows whose terms cancel
+    "tiny",                      # every V entry scaled by 2^-20
+])
+def test_v_magnitudes_far_from_one(values):
+    """V entries far from 1 in either direction still match the oracle.  The
+    P V product takes V as bf16 and P as bf16 hi + lo parts (P carried to
+    about 2^-17), so large entries in rows that cancel stay inside the
+    tolerance; a single fp16 rounding of P (2^-11) puts the second case
+    0.08 away from the oracle."""
     rng = np.random.default_rng(46)
     lens, news = [200, 90], [70, 90]
     q, kc, vc, tables, ctx, qsl = _case(rng, lens, news, 32, 8, 128, 16)
-    big = datagen.bf16_from_f32(np.array([3.0e5, -1.2e6, 7.0e4], np.float32))
-    # a few live slots of sequence 0 get huge V entries
-    for t, val in zip((5, 77, 150), big):
-        vc[tables[0][t // 16], 3, t % 16, 11] = val
+    if values == "tiny":
+        vc = datagen.bf16_from_f32((datagen.bf16_to_f32(vc) * 2.0 ** -20).astype(np.float32))
+    else:
+        vals = datagen.bf16_from_f32(np.array(values, np.float32))
+        # a few live slots of sequence 0 get the chosen V entries
+        for t, val in zip((5, 77, 150), vals):
+            vc[tables[0][t // 16], 3, t % 16, 11] = val
     got = _run(q, kc, vc, tables, ctx, qsl, 1.0 / math.sqrt(128))
     ref = paged_attention_prefill(q, kc, vc, tables, ctx, qsl, 1.0 / math.sqrt(128), "bf16")
     check_close(got, ref, "bf16")
