@@ -701,6 +701,19 @@ constexpr int kBWaves = 8;  // waves of a balanced-split workgroup (one per CU)
 constexpr int kTileBufs = 2;  // K/V tile buffers per wave (tiles in flight + 1)
 constexpr int kBThreads = kBWaves * kWave;
 
+// Workgroups are dispatched to the GPU's 8 XCDs in turn (workgroup b to XCD
+// b mod 8), and each XCD has its own L2.  Logical index of workgroup b of n
+// that gives each XCD one contiguous range of indices, so that neighbouring
+// shares (the samples of one prompt, next to each other in the sequence
+// list, read the same prompt blocks at the same time) run behind one L2.
+// A bijection of [0, n) for any n.
+__device__ inline int xcd_contiguous(int b, int n) {
+  constexpr int kXcds = 8;
+  const int q = n / kXcds, r = n - q * kXcds;
+  const int x = b % kXcds, i = b / kXcds;
+  return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
 // Number of the worker whose share [j T / n, (j + 1) T / n) holds item u.
 __device__ inline int worker_of(int64_t u, int64_t total, int32_t num_workers) {
   return (int)(((u + 1) * num_workers - 1) / total);
@@ -800,7 +813,8 @@ __global__ __launch_bounds__(kBThreads) void decode_balanced_kernel(
   // cover a sequence's chunk are exactly the range between its first and
   // last item's.
   const int ng = (int)min((int64_t)num_groups, total);
-  const int wg = blockIdx.x * kBWaves + wave;  // gs divides kBWaves: groups stay in a workgroup
+  // gs divides kBWaves: groups stay in a workgroup
+  const int wg = xcd_contiguous(blockIdx.x, gridDim.x) * kBWaves + wave;
   const int j = wg / gs;                       // this wave's group (worker)
   const int hi = wg - j * gs;                  // its head within the chunk
   if (j >= ng) return;  // no barrier follows: the waves are independent from here
