@@ -879,11 +879,11 @@ def run(args, cpu_pool):
         pkv.paged_kv_write(d["k"], d["v"], d["slots"], kc, vc, stream=stream)
         decode(i)
 
-    def decode(i):
+    def decode(i, on=stream):
         d = dsteps[i]
         pkv.paged_attention_decode(out, d["q"], kcs[i % R], vcs[i % R], d["tables"], d["ctx"],
                                    sh.scale, d["max_ctx"], args.partition_size,
-                                   workspace=workspace, stream=stream)
+                                   workspace=workspace, stream=on)
 
     for i in range(args.warmup):
         step(i)
@@ -919,6 +919,24 @@ def run(args, cpu_pool):
         b.record(stream)
     torch.cuda.synchronize()
     dec_med_ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+    # The same K calls recorded into one HIP graph and replayed: the host's
+    # launch work leaves the measurement, the GPU still runs both kernels of
+    # every call in stream order.
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        for i in timed_range(args):
+            decode(i, on=None)  # None: the capturing stream
+    torch.cuda.synchronize()
+    graph.replay()
+    ev8, ev9 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev8.record(stream)
+    graph.replay()
+    ev9.record(stream)
+    torch.cuda.synchronize()
+    dec_graph_ms = ev8.elapsed_time(ev9) / args.steps
+    del graph
 
     # Host-to-device upload of one step's inputs from pinned host memory (the
     # allocator's tables, lengths and slots, the queries and the new K/V),
@@ -996,10 +1014,13 @@ def run(args, cpu_pool):
                                 "between two HIP events on the launch stream",
                    "decode_ms_median": f"median of the same {args.steps} calls, each between "
                                        "its own pair of events",
+                   "decode_graph_ms": f"the same {args.steps} calls recorded into one HIP graph, "
+                                      "one replay between two events, divided by the call count",
                    "cold_caches": f"step i reads pool copy i mod {R}: the other copies stream "
                                   "at least 4x the 256 MiB Infinity Cache between two uses"},
         "decode_ms": round(dec_avg_ms, 4),
         "decode_ms_median": round(dec_med_ms, 4),
+        "decode_graph_ms": round(dec_graph_ms, 4),
         "upload_ms": round(upload_ms, 4),
         "upload_bytes": upload_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
