@@ -101,6 +101,58 @@ def roundtrip(c):
     return r
 
 
+def _random_op(rnd, c, o, ids, w=None):
+    """One random call on both allocators (add, fork, append, batched step or
+    free; ids may be unknown or repeated), results and error codes compared;
+    `w` (a ContentWorld) follows the slots when given."""
+    live = list(o.seqs)
+    r = rnd.random()
+    if r < 0.15:
+        s, n = rnd.choice(ids), rnd.randint(0, 3 * o.block_size + 1)
+        rc, ro, code = _both(lambda: c.add(s, n), lambda: o.add(s, n))
+        if code == 0:
+            assert rc.tolist() == ro
+            if w is not None:
+                w.on_add(s, ro)
+    elif r < 0.25:
+        p, ch = rnd.choice(ids), rnd.choice(ids)
+        _, _, code = _both(lambda: c.fork(p, ch), lambda: o.fork(p, ch))
+        if code == 0:
+            if w is not None:
+                w.on_fork(p, ch)
+    elif r < 0.45:
+        s = rnd.choice(ids)
+        rc, ro, code = _both(lambda: c.append(s), lambda: o.append(s))
+        if code == 0:
+            assert rc == ro
+            if ro[1] is not None:
+                if w is not None:
+                    w.on_copy(*ro[1])
+            if w is not None:
+                w.on_append(s, ro[0])
+    elif r < 0.85:
+        k = rnd.randint(0, max(1, len(live)))
+        batch = rnd.sample(live, min(k, len(live)))
+        if rnd.random() < 0.1:
+            batch.append(rnd.choice(ids))  # maybe unknown or repeated
+        rc, ro, code = _both(lambda: c.step(batch), lambda: o.step(batch))
+        if code == 0:
+            assert rc[0].tolist() == ro[0]
+            assert [tuple(x) for x in rc[1].tolist()] == ro[1]
+            for src, dst in ro[1]:
+                if w is not None:
+                    w.on_copy(src, dst)
+            for s, sl in zip(batch, ro[0]):
+                if w is not None:
+                    w.on_append(s, sl)
+    else:
+        s = rnd.choice(ids)
+        _, _, code = _both(lambda: c.free(s), lambda: o.free_seq(s))
+        if code == 0:
+            if w is not None:
+                w.on_free(s)
+
+
 @pytest.mark.parametrize("seed", range(40))
 def test_random_streams_match_oracle(seed):
     """Odd seeds also save and restore the allocator every 37 ops and continue
@@ -113,50 +165,31 @@ def test_random_streams_match_oracle(seed):
         if seed % 2 and step_no % 37 == 36:
             c = roundtrip(c)
             assert c.seq_ids() == sorted(o.seqs)
-        live = list(o.seqs)
-        r = rnd.random()
-        if r < 0.15:
-            s, n = rnd.choice(ids), rnd.randint(0, 3 * B + 1)
-            rc, ro, code = _both(lambda: c.add(s, n), lambda: o.add(s, n))
-            if code == 0:
-                assert rc.tolist() == ro
-                w.on_add(s, ro)
-        elif r < 0.25:
-            p, ch = rnd.choice(ids), rnd.choice(ids)
-            _, _, code = _both(lambda: c.fork(p, ch), lambda: o.fork(p, ch))
-            if code == 0:
-                w.on_fork(p, ch)
-        elif r < 0.45:
-            s = rnd.choice(ids)
-            rc, ro, code = _both(lambda: c.append(s), lambda: o.append(s))
-            if code == 0:
-                assert rc == ro
-                if ro[1] is not None:
-                    w.on_copy(*ro[1])
-                w.on_append(s, ro[0])
-        elif r < 0.85:
-            k = rnd.randint(0, max(1, len(live)))
-            batch = rnd.sample(live, min(k, len(live)))
-            if rnd.random() < 0.1:
-                batch.append(rnd.choice(ids))  # maybe unknown or repeated
-            rc, ro, code = _both(lambda: c.step(batch), lambda: o.step(batch))
-            if code == 0:
-                assert rc[0].tolist() == ro[0]
-                assert [tuple(x) for x in rc[1].tolist()] == ro[1]
-                for src, dst in ro[1]:
-                    w.on_copy(src, dst)
-                for s, sl in zip(batch, ro[0]):
-                    w.on_append(s, sl)
-        else:
-            s = rnd.choice(ids)
-            _, _, code = _both(lambda: c.free(s), lambda: o.free_seq(s))
-            if code == 0:
-                w.on_free(s)
+        _random_op(rnd, c, o, ids, w)
         live = list(o.seqs)
         _same_state(c, o, live)
         fifo, ref = c.export()
         tables = {s: o.table(s) for s in live}
         check(w, tables, {s: o.length(s) for s in live}, ref, fifo)
+
+
+def test_ten_thousand_short_streams():
+    """10^4 seeded streams of 48 random calls each: every call's result and
+    error code compared, and the whole state (free-list order, reference
+    counts, tables, lengths) at the end of each stream."""
+    for k in range(10_000):
+        seed = 100_000 + k
+        rnd, B, N, order, ids = _random_stream(seed)
+        c = pkv.BlockAllocator(N, B, order)
+        o = BlockAllocatorModel(N, B, order)
+        try:
+            for _ in range(48):
+                _random_op(rnd, c, o, ids)
+            _same_state(c, o, list(o.seqs))
+        except AssertionError as e:
+            raise AssertionError(f"stream seed {seed}: {e}") from e
+        finally:
+            c.close()
 
 
 def test_stats_counts_shared_blocks_once():

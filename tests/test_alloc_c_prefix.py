@@ -47,9 +47,12 @@ def test_enable_only_before_the_first_sequence():
     assert d.cache_stats()["enabled"] == 0 and d.cached_blocks([1, 2]) == []
 
 
-@pytest.mark.parametrize("seed", range(16))
-def test_random_streams_match_oracle(seed):
-    rng = random.Random(1000 + seed)
+def _stream(rng, steps, restore_every=0, check_every_step=True):
+    """A random stream of prompt admissions (token ids, often sharing a live
+    sequence's prefix), forks, id-less admissions, batched steps with or
+    without ids, single appends and frees on both allocators; every call's
+    result and error code compared, the state after every call (or after the
+    last), and a lookup of a random prompt each time the state is compared."""
     B = rng.choice([1, 2, 4, 16])
     N = rng.randrange(3, 40)
     order = rng.sample(range(N), N)
@@ -58,9 +61,9 @@ def test_random_streams_match_oracle(seed):
     alphabet = list(range(rng.choice([2, 3, 50])))
     hist = {}
     nid = 0
-    for step_no in range(300):
-        if seed % 2 and step_no % 29 == 28:  # continue on a restored handle
-            c = roundtrip(c)
+    for step_no in range(steps):
+        if restore_every and step_no % restore_every == restore_every - 1:
+            c = roundtrip(c)  # continue on a restored handle
         live = sorted(o.seqs)
         r = rng.random()
         if r < 0.3 or not live:
@@ -110,6 +113,8 @@ def test_random_streams_match_oracle(seed):
             _both(lambda: c.free(s), lambda: o.free_seq(s))
             del hist[s]
         live = sorted(o.seqs)
+        if not check_every_step and step_no + 1 < steps:
+            continue
         _same_state(c, o, live)
         assert _stats(c) == o.cache_stats()
         probe = [rng.choice(alphabet) for _ in range(rng.randrange(0, 4 * B + 1))]
@@ -117,8 +122,26 @@ def test_random_streams_match_oracle(seed):
             h = [t for t in hist[rng.choice(live)] if t is not None]
             probe = h[:rng.randrange(0, len(h) + 1)] + probe[:2]
         assert c.cached_blocks(probe) == o.cached_blocks(probe)
-    st = o.cache_stats()
+    c.close()
+    return o.cache_stats()
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_streams_match_oracle(seed):
+    """Odd seeds continue on a restored handle every 29 calls."""
+    st = _stream(random.Random(1000 + seed), 300, restore_every=29 if seed % 2 else 0)
     assert st["queries"] > 0
+
+
+def test_ten_thousand_short_streams():
+    """10^4 seeded streams of 24 calls each, every call compared and the whole
+    state (and a prompt lookup) at the end of each stream."""
+    for k in range(10_000):
+        seed = 200_000 + k
+        try:
+            _stream(random.Random(seed), 24, check_every_step=False)
+        except AssertionError as e:
+            raise AssertionError(f"stream seed {seed}: {e}") from e
 
 
 def test_hit_chain_survives_hash_table_deletions():

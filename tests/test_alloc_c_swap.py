@@ -56,9 +56,11 @@ def test_errors_match():
     _same_host(c, o)
 
 
-@pytest.mark.parametrize("seed", range(16))
-def test_random_streams_match_oracle(seed):
-    rng = random.Random(300 + seed)
+def _stream(rng, steps, restore_every=0, check_every_step=True):
+    """A random stream of admissions, forks, batched steps, swap-outs and
+    swap-ins of groups (ids may be live, swapped or repeated) and frees on both
+    allocators; every call's result and error code compared, the device and
+    host state after every call (or after the last)."""
     B = rng.choice([1, 2, 4, 16])
     N, H = rng.randrange(4, 40), rng.randrange(2, 40)
     order, horder = rng.sample(range(N), N), rng.sample(range(H), H)
@@ -68,9 +70,9 @@ def test_random_streams_match_oracle(seed):
     c.set_host_pool(H, horder)
     o.set_host_pool(H, horder)
     nid = 0
-    for step_no in range(300):
-        if seed % 2 and step_no % 29 == 28:  # continue on a restored handle
-            c = roundtrip(c)
+    for step_no in range(steps):
+        if restore_every and step_no % restore_every == restore_every - 1:
+            c = roundtrip(c)  # continue on a restored handle
         live, out = sorted(o.seqs), sorted(o.swapped)
         r = rng.random()
         if r < 0.2 or not (live or out):
@@ -103,8 +105,28 @@ def test_random_streams_match_oracle(seed):
             s = rng.choice(live + out)
             _both(lambda: c.free(s), lambda: o.free_seq(s))
         live = sorted(o.seqs)
+        if not check_every_step and step_no + 1 < steps:
+            continue
         _same_state(c, o, live)
         _same_host(c, o)
         for s in sorted(o.swapped):
             assert c.swapped(s)
         assert c.stats()["num_seqs"] == len(o.seqs) + len(o.swapped)
+    c.close()
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_streams_match_oracle(seed):
+    """Odd seeds continue on a restored handle every 29 calls."""
+    _stream(random.Random(300 + seed), 300, restore_every=29 if seed % 2 else 0)
+
+
+def test_ten_thousand_short_streams():
+    """10^4 seeded streams of 24 calls each, every call compared and the
+    device and host state at the end of each stream."""
+    for k in range(10_000):
+        seed = 300_000 + k
+        try:
+            _stream(random.Random(seed), 24, check_every_step=False)
+        except AssertionError as e:
+            raise AssertionError(f"stream seed {seed}: {e}") from e
