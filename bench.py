@@ -937,6 +937,26 @@ def run(args, cpu_pool):
     torch.cuda.synchronize()
     dec_graph_ms = ev8.elapsed_time(ev9) / args.steps
     del graph
+    # Flushed: 50 calls (the timed steps' inputs in turn), each after an
+    # untimed read of a 1 GiB buffer on the stream, so L2 and the Infinity
+    # Cache hold none of its K/V when it starts, only clean lines of that
+    # buffer (a write would leave them dirty, and the call would then also
+    # pay for their write-back); median of the 50.
+    flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+    fsum = torch.zeros((), dtype=torch.int64, device="cuda")
+    for _ in range(3):  # read passes evict the lines the fill left dirty
+        torch.sum(flush, dim=0, dtype=torch.int64, out=fsum)
+    fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(50)]
+    torch.cuda.synchronize()
+    for r, (a, b) in enumerate(fev):
+        torch.sum(flush, dim=0, dtype=torch.int64, out=fsum)
+        a.record(stream)
+        decode(args.warmup + r % args.steps)
+        b.record(stream)
+    torch.cuda.synchronize()
+    dec_flush_ms = float(np.median([a.elapsed_time(b) for a, b in fev]))
+    del flush, fsum
 
     # Host-to-device upload of one step's inputs from pinned host memory (the
     # allocator's tables, lengths and slots, the queries and the new K/V),
@@ -1016,11 +1036,14 @@ def run(args, cpu_pool):
                                        "its own pair of events",
                    "decode_graph_ms": f"the same {args.steps} calls recorded into one HIP graph, "
                                       "one replay between two events, divided by the call count",
+                   "decode_ms_flushed": "median of 50 calls, each between its own pair of events "
+                                        "after an untimed read of a 1 GiB buffer on the stream",
                    "cold_caches": f"step i reads pool copy i mod {R}: the other copies stream "
                                   "at least 4x the 256 MiB Infinity Cache between two uses"},
         "decode_ms": round(dec_avg_ms, 4),
         "decode_ms_median": round(dec_med_ms, 4),
         "decode_graph_ms": round(dec_graph_ms, 4),
+        "decode_ms_flushed": round(dec_flush_ms, 4),
         "upload_ms": round(upload_ms, 4),
         "upload_bytes": upload_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
