@@ -400,6 +400,10 @@ int pkv_alloc_export(const pkv_alloc* a, int32_t* free_fifo_out, int32_t* num_fr
                      int32_t* ref_cnt_out);
 
 /*
+ * The pages say nothing about saving an allocator; these calls exist so that
+ * a process can persist, move or replay the manager's state (and a test can
+ * compare it word for word with a reference model).
+ *
  * Checkpoint and restore of the whole allocator state: free-list order,
  * reference counts, every live sequence (id, length, block table, and the
  * token ids and chain hash it enters prefix-cache blocks with), the prefix
