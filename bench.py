@@ -288,10 +288,11 @@ PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic.json")
 PREFILL_SOURCE = os.path.join(ROOT, "paged_kv_cache_377_amd", "csrc", "prefill.hip")
 
 
-def recorded_traffic(record: str, source: str, sha_key: str, **config):
-    """HBM bytes per call from a committed record of rocprofv3 FETCH_SIZE /
-    WRITE_SIZE runs (scaled by the copy calibration), or None when there is no
-    such run for this configuration or the kernel source has changed since."""
+def recorded_traffic(record: str, source: str, sha_key: str, kernel=None, **config):
+    """HBM bytes per call (or, with `kernel`, per launch of that kernel) from a
+    committed record of rocprofv3 FETCH_SIZE / WRITE_SIZE runs (scaled by the
+    copy calibration), or None when there is no such run for this configuration
+    or the kernel source has changed since."""
     import hashlib
 
     try:
@@ -303,13 +304,17 @@ def recorded_traffic(record: str, source: str, sha_key: str, **config):
         return None
     if rec.get(sha_key) != sha or any(rec.get(k) != v for k, v in config.items()):
         return None
+    if kernel is not None:
+        return int(round((rec["fetch_kib"][kernel] * rec["fetch_scale"]
+                          + rec["write_kib"][kernel] * rec["write_scale"]) * 1024))
     return int(rec["hbm_bytes_per_call"])
 
 
-def measured_traffic(workload: int, block_size, partition_size: int):
-    """HBM bytes per decode call (see recorded_traffic)."""
-    return recorded_traffic(TRAFFIC_FILE, DECODE_SOURCE, "decode_source_sha256", workload=workload,
-                            block_size=block_size or 16, partition_size=partition_size)
+def measured_traffic(workload: int, block_size, partition_size: int, kernel=None):
+    """HBM bytes per decode call, or per launch of `kernel` (see recorded_traffic)."""
+    return recorded_traffic(TRAFFIC_FILE, DECODE_SOURCE, "decode_source_sha256", kernel=kernel,
+                            workload=workload, block_size=block_size or 16,
+                            partition_size=partition_size)
 
 
 MALL_BYTES = 256 << 20  # MI355X Infinity Cache (memory-side, in front of HBM)
@@ -919,6 +924,21 @@ def run(args, cpu_pool):
         b.record(stream)
     torch.cuda.synchronize()
     dec_med_ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+    # The dominant kernel alone: the same calls once more, each with a pair of
+    # events that the library records on the stream right around its first
+    # kernel (the balanced split, or the partition kernel), so the combine
+    # launch stays outside; mean over the calls.
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in timed_range(args)]
+    for a, b in kev:  # torch creates an event when it is first recorded
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    for (a, b), i in zip(kev, timed_range(args)):
+        pkv.decode_mark_next_call(a, b)
+        decode(i)
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in kev]))
     # The same K calls recorded into one HIP graph and replayed: the host's
     # launch work leaves the measurement, the GPU still runs both kernels of
     # every call in stream order.
@@ -999,7 +1019,11 @@ def run(args, cpu_pool):
     alg = sum(wl.algorithmic_bytes(i) for i in timed)
     ms_per_step = wall * 1e3 / args.steps
     value = kv / (wall) / 1e9
-    achieved = alg / args.steps / (dec_avg_ms * 1e-3) / 1e9
+    call_achieved = alg / args.steps / (dec_avg_ms * 1e-3) / 1e9
+    # the dominant kernel's algorithmic bytes: 2 D sizeof(dtype) per
+    # (sequence, KV head, context token), the K and V rows it reads
+    kern_bytes = kv / args.steps
+    achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
     res = {
         "metric": "paged-decode KV-read GB/s",
         "value": round(value, 1),
@@ -1034,6 +1058,9 @@ def run(args, cpu_pool):
                                 "between two HIP events on the launch stream",
                    "decode_ms_median": f"median of the same {args.steps} calls, each between "
                                        "its own pair of events",
+                   "roofline.kernel_ms": f"mean of the same {args.steps} calls' first kernel, "
+                                         "each between a pair of events the library records "
+                                         "on the launch stream right around that launch",
                    "decode_graph_ms": f"the same {args.steps} calls recorded into one HIP graph, "
                                       "one replay between two events, divided by the call count",
                    "decode_ms_flushed": "median of 50 calls, each between its own pair of events "
@@ -1049,9 +1076,18 @@ def run(args, cpu_pool):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(args.workload, args.block_size,
-                                                 args.partition_size),
-                     "kernel": "paged_attention_decode (partition + reduce launches)",
-                     "algorithmic_bytes_per_launch": int(alg / args.steps)},
+                                                 args.partition_size, kernel="decode_balanced"),
+                     "kernel": "decode_balanced_kernel (the decode call's first launch; "
+                               "its combine launch is in `call`)",
+                     "kernel_ms": round(kern_ms, 4),
+                     "algorithmic_bytes_per_launch": int(kern_bytes),
+                     "call": {"achieved": round(call_achieved, 1),
+                              "frac": round(call_achieved / HBM_PEAK_GBPS, 4),
+                              "ms": round(dec_avg_ms, 4),
+                              "algorithmic_bytes": int(alg / args.steps),
+                              "traffic": measured_traffic(args.workload, args.block_size,
+                                                          args.partition_size),
+                              "launches": "balanced split + combine"}},
         "allocator_us_per_step": None,
     }
     if args.workload in (3, 6):

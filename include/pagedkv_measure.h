@@ -1,5 +1,5 @@
 /*
- * pagedkv_measure.h -- measurement call of libpagedkv.so (not part of the
+ * pagedkv_measure.h -- measurement calls of libpagedkv.so (not part of the
  * attention path).
  *
  * The decode is bound by the gather of K and V rows from scattered physical
@@ -40,6 +40,26 @@ extern "C" {
 int pkv_measure_gather(const void* k_pool, const void* v_pool, const pkv_cache_desc* c,
                        const int32_t* runs, int64_t num_runs, int32_t num_workers,
                        int32_t runs_in_flight, uint32_t* sink, void* stream);
+
+/*
+ * Time one kernel of a decode call.  A decode call launches two kernels (the
+ * partition or balanced-split kernel, then the combine or reduce kernel when
+ * the split needs one), so events placed around the call time both.  After
+ * this call, the next decode call made from the same thread (any of
+ * pkv_paged_attention_decode, pkv_paged_attention_decode_append,
+ * pkv_paged_attention_decode_noalloc) records `before` on its stream right
+ * before its first kernel and `after` right after it; that call clears the
+ * pair whatever it returns, and a call that launches nothing (an error, no
+ * sequences) records neither.  The calls after it record nothing until the
+ * next pkv_decode_mark_next_call.
+ *
+ *   before, after   hipEvent_t handles created by the caller (both, or both
+ *                   NULL to clear a pending pair)
+ * Not for use while the stream is being captured into a graph.  Errors:
+ * PKV_EINVAL (exactly one NULL); a failed record returns PKV_EHIP from the
+ * decode call.
+ */
+int pkv_decode_mark_next_call(void* before, void* after);
 
 #ifdef __cplusplus
 }

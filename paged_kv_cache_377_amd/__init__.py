@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     cache_desc,
     copy_blocks,
     decode_balanced_max_seqs,
+    decode_mark_next_call,
     decode_workspace_bytes,
     header_functions,
     lib,

@@ -104,6 +104,7 @@ _SIGS = {
     "pkv_swap_blocks": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _P(CacheDesc), _vp, _i32, _vp]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_measure_gather": (_i32, [_vp, _vp, _P(CacheDesc), _vp, _i64, _i32, _i32, _vp, _vp]),
+    "pkv_decode_mark_next_call": (_i32, [_vp, _vp]),
 }
 
 _lib = None
@@ -401,6 +402,26 @@ def measure_gather(k_pool, v_pool, runs, num_workers: int, runs_in_flight: int, 
     _check(lib().pkv_measure_gather(_ptr(k_pool), _ptr(v_pool), ctypes.byref(desc), _ptr(runs),
                                     runs.numel(), int(num_workers), int(runs_in_flight),
                                     _ptr(sink), _stream(stream)))
+
+
+def decode_mark_next_call(before, after) -> None:
+    """The next call into the library's decode on this thread records the
+    events ``before`` and ``after`` (torch.cuda.Event, each recorded once
+    already so that it exists) on its stream around its first kernel (the
+    balanced-split or partition kernel), and clears them whatever it returns;
+    ``None, None`` clears a pending pair."""
+    if (before is None) != (after is None):
+        raise PagedKVError(PKV_EINVAL, "give both events or neither")
+
+    def handle(ev):
+        if ev is None:
+            return None
+        h = int(ev.cuda_event)
+        if not h:
+            raise PagedKVError(PKV_EINVAL, "record the event once before marking with it")
+        return h
+
+    _check(lib().pkv_decode_mark_next_call(handle(before), handle(after)))
 
 
 # --------------------------------------------------------- host checks

@@ -50,6 +50,7 @@
 #include <mutex>
 #include <type_traits>
 
+#include "pagedkv_measure.h"
 #include "pkv_internal.h"
 
 namespace {
@@ -1224,7 +1225,21 @@ struct LaunchArgs {
   float* part_ml;
   float* part_o;
   hipStream_t stream;
+  hipEvent_t mark_before;  // non-null: recorded around the first kernel
+  hipEvent_t mark_after;
 };
+
+// Events the next decode call on this thread records around its first
+// kernel (pkv_decode_mark_next_call); each call takes them and clears them.
+thread_local hipEvent_t t_mark_before = nullptr;
+thread_local hipEvent_t t_mark_after = nullptr;
+
+int record_mark(hipEvent_t e, hipStream_t st) {
+  if (!e) return PKV_OK;
+  const hipError_t r = hipEventRecord(e, st);
+  if (r != hipSuccess) return pkv__fail(PKV_EHIP, "hipEventRecord: %s", hipGetErrorString(r));
+  return PKV_OK;
+}
 
 int check_launch(const char* what) {
   const hipError_t e = hipGetLastError();
@@ -1239,6 +1254,8 @@ int launch(const LaunchArgs& a) {
       const size_t lds = (size_t)(2 * a.num_seqs + 1) * sizeof(int32_t);
       const int32_t groups = a.plan.workers / a.plan.gs;
       const dim3 grid((uint32_t)(a.plan.workers / kBWaves));
+      int rc = record_mark(a.mark_before, a.stream);
+      if (rc) return rc;
       if (a.k_new)
         hipLaunchKernelGGL((decode_balanced_kernel<D, B, G, true>), grid, dim3(kBThreads), lds,
                            a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
@@ -1254,7 +1271,8 @@ int launch(const LaunchArgs& a) {
                            (uint16_t*)a.out, a.meta, a.part_ml, a.part_o, a.num_seqs,
                            a.num_kv_heads, a.num_blocks, a.max_context_len, groups, a.plan.gs,
                            a.qscale, nullptr, nullptr, nullptr, nullptr);
-      int rc = check_launch("decode_balanced");
+      rc = check_launch("decode_balanced");
+      if (!rc) rc = record_mark(a.mark_after, a.stream);
       if (rc) return rc;
       const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * G;
       hipLaunchKernelGGL((decode_balanced_reduce_kernel<D, G>),
@@ -1267,6 +1285,8 @@ int launch(const LaunchArgs& a) {
   }
   const int64_t grid = (int64_t)a.num_seqs * a.num_kv_heads * a.plan.parts;
   if (grid > INT32_MAX) return pkv__fail(PKV_EINVAL, "decode grid too large");
+  int rc = record_mark(a.mark_before, a.stream);
+  if (rc) return rc;
   if constexpr (E::bytes == 2) {
     hipLaunchKernelGGL((decode_partition_mfma_kernel<D, B, G>), dim3((uint32_t)grid),
                        dim3(kThreads), 0, a.stream, (const uint16_t*)a.q,
@@ -1282,7 +1302,8 @@ int launch(const LaunchArgs& a) {
                        a.num_seqs, a.num_kv_heads, a.num_blocks, a.plan.parts, a.plan.ps,
                        a.max_context_len, a.qscale);
   }
-  int rc = check_launch("decode_partition");
+  rc = check_launch("decode_partition");
+  if (!rc) rc = record_mark(a.mark_after, a.stream);
   if (rc) return rc;
   if (a.plan.parts > 1) {
     hipLaunchKernelGGL((decode_reduce_kernel<E, D>), dim3((uint32_t)(a.num_seqs * a.num_q_heads)),
@@ -1356,6 +1377,15 @@ extern "C" size_t pkv_decode_workspace_bytes(const pkv_cache_desc* c, int32_t nu
   return pl.bytes;
 }
 
+extern "C" int pkv_decode_mark_next_call(void* before, void* after) {
+  pkv__clear_error();
+  if ((before == nullptr) != (after == nullptr))
+    return pkv__fail(PKV_EINVAL, "give both events or neither");
+  t_mark_before = (hipEvent_t)before;
+  t_mark_after = (hipEvent_t)after;
+  return PKV_OK;
+}
+
 extern "C" int32_t pkv_decode_balanced_max_seqs(void) {
   pkv__clear_error();
   DeviceLimits lim;
@@ -1371,6 +1401,9 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
                 const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                 int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
                 size_t workspace_bytes, void* stream) {
+  // the marks belong to this call, whatever it returns
+  const hipEvent_t mark_before = t_mark_before, mark_after = t_mark_after;
+  t_mark_before = t_mark_after = nullptr;
   int rc = check_sizes(c, num_seqs, num_q_heads, max_context_len, partition_size);
   if (rc) return rc;
   if (max_blocks_per_seq < 0 || (int64_t)max_blocks_per_seq * c->block_size < max_context_len)
@@ -1439,6 +1472,8 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
   a.part_ml = pl.bytes ? (float*)(ws + pl.ml_off) : nullptr;
   a.part_o = pl.bytes ? (float*)(ws + pl.o_off) : nullptr;
   a.stream = (hipStream_t)stream;
+  a.mark_before = mark_before;
+  a.mark_after = mark_after;
   const int G = num_q_heads / c->num_kv_heads;
   if (c->dtype == PKV_BF16) return dispatch_d<BF16>(a, c->head_dim, c->block_size, G);
   return dispatch_d<F32>(a, c->head_dim, c->block_size, G);
@@ -1507,10 +1542,12 @@ extern "C" int pkv_paged_attention_decode_noalloc(
     int32_t partition_size, void* stream) {
   pkv__clear_error();
   int rc = check_sizes(c, num_seqs, num_q_heads, max_context_len, partition_size);
+  if (rc || num_seqs == 0) t_mark_before = t_mark_after = nullptr;  // no launch follows
   if (rc) return rc;
   if (num_seqs == 0) return PKV_OK;
   Plan pl;
   rc = make_plan(c, num_seqs, num_q_heads, max_context_len, partition_size, &pl);
+  if (rc || pl.bytes > kScratchBytes) t_mark_before = t_mark_after = nullptr;
   if (rc) return rc;
   if (pl.bytes > kScratchBytes)
     return pkv__fail(PKV_EINVAL,
@@ -1520,7 +1557,10 @@ extern "C" int pkv_paged_attention_decode_noalloc(
   void* ws = nullptr;
   if (pl.bytes) {
     rc = scratch_address(&ws);
-    if (rc) return rc;
+    if (rc) {
+      t_mark_before = t_mark_after = nullptr;
+      return rc;
+    }
   }
   return decode_impl(out, q, nullptr, nullptr, k_cache, v_cache, c, block_tables,
                      max_blocks_per_seq, context_lens, num_seqs, num_q_heads, max_context_len,

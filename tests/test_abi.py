@@ -1,6 +1,8 @@
 """The C-ABI library loads on a machine without a GPU, exports every function
 include/pagedkv.h declares, and its host-side checks behave (no device calls)."""
 
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -71,3 +73,14 @@ def test_bad_descriptor_rejected_without_gpu():
     assert e.value.code == pkv.PKV_EINVAL
     with pytest.raises(pkv.PagedKVError):
         pkv.validate_copy([[0, 1]], pkv.CacheDesc(4, 2, 8, 64, 7))
+
+
+def test_decode_marks_need_both_events():
+    """Argument check of the decode's event hook (host only, no event is
+    touched): one event without the other is refused, none clears."""
+    f = pkv.lib().pkv_decode_mark_next_call
+    assert f(ctypes.c_void_p(8), None) == pkv.PKV_EINVAL
+    assert f(None, ctypes.c_void_p(8)) == pkv.PKV_EINVAL
+    assert f(None, None) == pkv.PKV_OK
+    with pytest.raises(pkv.PagedKVError):
+        pkv.decode_mark_next_call(object(), None)

@@ -320,3 +320,52 @@ def test_balanced_workspace_reused_across_calls():
         torch.cuda.synchronize()
         ref = paged_attention_decode(q, kc, vc, tables, ctx, 1.0 / math.sqrt(D), "bf16")
         print("rep", rep, check_close(host(out), ref, "bf16"))
+
+
+@pytest.mark.parametrize("ps", [AUTO, 64])
+def test_marked_events_bracket_the_first_kernel(ps):
+    """pkv_decode_mark_next_call: the next call records the events right
+    around its first kernel only (inside the call's own span), once; a call
+    that fails clears the pair; outputs do not change."""
+    q, kc, vc, tables, ctx, scale = _small_case("bf16", 128, 16, 4, 13,
+                                                lens=[4096, 3000, 2049, 1000, 777, 100])
+    dq, dkc, dvc, dt, dc = dev(q), dev(kc), dev(vc), dev(tables), dev(ctx)
+    out = torch.empty_like(dq)
+    mx = int(ctx.max())
+
+    def call():
+        pkv.paged_attention_decode(out, dq, dkc, dvc, dt, dc, scale, mx, ps)
+
+    call()
+    torch.cuda.synchronize()
+    plain = host(out)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev:  # create them
+        e.record()
+    c0, c1, a, b = ev
+    torch.cuda.synchronize()
+    c0.record()
+    pkv.decode_mark_next_call(a, b)
+    call()
+    c1.record()
+    torch.cuda.synchronize()
+    t_kernel, t_call = a.elapsed_time(b), c0.elapsed_time(c1)
+    print(f"ps={ps}: first kernel {t_kernel:.4f} ms of a {t_call:.4f} ms call", flush=True)
+    assert 0.0 < t_kernel <= t_call
+    assert 0.0 <= c0.elapsed_time(a) and 0.0 <= b.elapsed_time(c1)
+    assert np.array_equal(host(out), plain)
+    # used once: an unmarked call leaves the pair where it was
+    call()
+    torch.cuda.synchronize()
+    assert a.elapsed_time(b) == t_kernel
+    # a failing call takes the pair with it (a workspace is passed, so the
+    # binding hands the bad partition size to the library, which refuses it)
+    pkv.decode_mark_next_call(a, b)
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(pkv.PagedKVError):
+        pkv.paged_attention_decode(out, dq, dkc, dvc, dt, dc, scale, mx, -7, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    assert a.elapsed_time(b) == t_kernel
+    with pytest.raises(pkv.PagedKVError):
+        pkv.decode_mark_next_call(a, None)
