@@ -328,6 +328,10 @@ typedef struct {
   double utilization;        /* filled_slots / allocated_slots (0 if none)      */
 } pkv_stats;
 
+/* Largest block size the allocator accepts (the kernels are built for 8, 16
+ * and 32). */
+#define PKV_MAX_BLOCK_SIZE 65536
+
 /*
  * New pool of `num_blocks` blocks of `block_size` tokens.  free_order: host
  * [num_blocks] permutation of 0..num_blocks-1 giving the free list from head

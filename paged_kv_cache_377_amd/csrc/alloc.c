@@ -314,9 +314,9 @@ static int no_blocks(const pkv_alloc* a, int64_t needed) {
 
 pkv_alloc* pkv_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order) {
   pkv__clear_error();
-  if (num_blocks <= 0 || block_size <= 0) {
-    pkv__fail(PKV_EINVAL, "num_blocks (%d) and block_size (%d) must be positive",
-              num_blocks, block_size);
+  if (num_blocks <= 0 || block_size <= 0 || block_size > PKV_MAX_BLOCK_SIZE) {
+    pkv__fail(PKV_EINVAL, "num_blocks (%d) must be positive and block_size (%d) in 1..%d",
+              num_blocks, block_size, PKV_MAX_BLOCK_SIZE);
     return NULL;
   }
   pkv_alloc* a = (pkv_alloc*)calloc(1, sizeof *a);
@@ -1159,11 +1159,16 @@ pkv_alloc* pkv_alloc_restore(const void* buf, size_t bytes) {
   const int32_t nfree = (int32_t)rd(&r, 0, N);
   const int64_t nseq = rd(&r, 0, INT32_MAX);
   const int32_t ncached = (int32_t)rd(&r, 0, N);
-  const int64_t hits = rd(&r, 0, INT64_MAX);
-  const int64_t queries = rd(&r, 0, INT64_MAX);
-  const int64_t evictions = rd(&r, 0, INT64_MAX);
+  /* counters below 2^62 leave every later increment room */
+  const int64_t kCounterMax = (int64_t)1 << 62;
+  const int64_t hits = rd(&r, 0, kCounterMax);
+  const int64_t queries = rd(&r, 0, kCounterMax);
+  const int64_t evictions = rd(&r, 0, kCounterMax);
   const int32_t hnfree = (int32_t)rd(&r, 0, H);
-  if (r.bad || (!prefix && ncached)) {
+  /* every device and host block's reference count is one word of the state,
+   * so the pools cannot be larger than the words present */
+  if (r.bad || (!prefix && ncached) || hits > queries || B > PKV_MAX_BLOCK_SIZE ||
+      (int64_t)N + H > (int64_t)r.n) {
     pkv__fail(PKV_EINVAL, "saved state has a bad header");
     return NULL;
   }
