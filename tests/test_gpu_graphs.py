@@ -110,6 +110,46 @@ def test_decode_step_graph_replays_match_eager():
                 assert np.array_equal(v_after[blk, :, t % B], vn[s])
 
 
+@pytest.mark.parametrize("partition_size", [pkv.PKV_PARTITION_AUTO, 128])
+def test_noalloc_decode_graph_replays_match_eager(partition_size):
+    """The allocation-free decode (its workspace is the library's scratch
+    array) recorded into a graph: every replay, with new queries and eager
+    calls of both entry points in between, matches the workspace entry point
+    bit for bit."""
+    rng = np.random.default_rng(74 + max(partition_size, 0))
+    lens = [900, 33, 2048, 1, 500, 129]
+    hq, hkv, D, B = 32, 8, 128, 16
+    print(f"graph noalloc decode lens={lens} partition_size={partition_size}", flush=True)
+    kc, vc, tables, ctx, used, free = _pool(rng, lens, hkv, D, B)
+    S = len(lens)
+    scale = 1.0 / np.sqrt(D)
+    mx = int(ctx.max())
+    s_kc, s_vc, s_tab, s_ctx = dev(kc), dev(vc), dev(tables), dev(ctx)
+    s_q = dev(datagen.normal(rng, (S, hq, D), "bf16"))
+    s_out = torch.empty_like(s_q)
+
+    g = _capture(lambda: pkv.paged_attention_decode_noalloc(s_out, s_q, s_kc, s_vc, s_tab, s_ctx,
+                                                            scale, mx, partition_size))
+    for rep in range(3):
+        q = datagen.normal(rng, (S, hq, D), "bf16")
+        s_q.copy_(dev(q))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e_out = torch.empty_like(s_q)
+        pkv.paged_attention_decode(e_out, dev(q), s_kc, s_vc, s_tab, s_ctx, scale, mx,
+                                   partition_size)
+        n_out = torch.empty_like(s_q)
+        pkv.paged_attention_decode_noalloc(n_out, dev(q), s_kc, s_vc, s_tab, s_ctx, scale, mx,
+                                           partition_size)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(s_out), host(e_out)), f"replay {rep}: differs from eager"
+        assert np.array_equal(host(n_out), host(e_out))
+        if rep == 2:
+            ref = paged_attention_decode(q, kc, vc, tables, ctx, scale, "bf16")
+            check_close(host(s_out), ref, "bf16")
+
+
 @pytest.mark.parametrize("partition_size", [pkv.PKV_PARTITION_AUTO, 256])
 def test_write_then_decode_graph_replays_match_eager(partition_size):
     """paged_kv_write of new tokens + decode (balanced split or split-context)."""
