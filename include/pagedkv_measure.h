@@ -47,16 +47,17 @@ int pkv_measure_gather(const void* k_pool, const void* v_pool, const pkv_cache_d
  * the split needs one), so events placed around the call time both.  After
  * this call, the next decode call made from the same thread (any of
  * pkv_paged_attention_decode, pkv_paged_attention_decode_append,
- * pkv_paged_attention_decode_noalloc) records `before` on its stream right
- * before its first kernel and `after` right after it; that call clears the
- * pair whatever it returns, and a call that launches nothing (an error, no
+ * pkv_paged_attention_decode_noalloc) launches its first kernel with
+ * hipExtLaunchKernel and the pair as that launch's start and stop events, so
+ * they hold the kernel's own start and end; that call clears the pair
+ * whatever it returns, and a call that launches nothing (an error, no
  * sequences) records neither.  The calls after it record nothing until the
  * next pkv_decode_mark_next_call.
  *
  *   before, after   hipEvent_t handles created by the caller (both, or both
  *                   NULL to clear a pending pair)
  * Not for use while the stream is being captured into a graph.  Errors:
- * PKV_EINVAL (exactly one NULL); a failed record returns PKV_EHIP from the
+ * PKV_EINVAL (exactly one NULL); a failed launch returns PKV_EHIP from the
  * decode call.
  */
 int pkv_decode_mark_next_call(void* before, void* after);

@@ -405,11 +405,11 @@ def measure_gather(k_pool, v_pool, runs, num_workers: int, runs_in_flight: int, 
 
 
 def decode_mark_next_call(before, after) -> None:
-    """The next call into the library's decode on this thread records the
-    events ``before`` and ``after`` (torch.cuda.Event, each recorded once
-    already so that it exists) on its stream around its first kernel (the
-    balanced-split or partition kernel), and clears them whatever it returns;
-    ``None, None`` clears a pending pair."""
+    """The next call into the library's decode on this thread launches its
+    first kernel (the balanced-split or partition kernel) with ``before`` and
+    ``after`` (torch.cuda.Event, each recorded once already so that it exists)
+    as the launch's start and stop events, and clears them whatever it
+    returns; ``None, None`` clears a pending pair."""
     if (before is None) != (after is None):
         raise PagedKVError(PKV_EINVAL, "give both events or neither")
 

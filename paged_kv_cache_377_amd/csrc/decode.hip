@@ -40,6 +40,7 @@
 // exponentials are exp2, output rounded to the cache dtype (bf16:
 // round-to-nearest-even).  Masked tokens are selected out, never multiplied
 // by zero, so NaN bits in unfilled slots cannot reach the result.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -1234,11 +1235,15 @@ struct LaunchArgs {
 thread_local hipEvent_t t_mark_before = nullptr;
 thread_local hipEvent_t t_mark_after = nullptr;
 
-int record_mark(hipEvent_t e, hipStream_t st) {
-  if (!e) return PKV_OK;
-  const hipError_t r = hipEventRecord(e, st);
-  if (r != hipSuccess) return pkv__fail(PKV_EHIP, "hipEventRecord: %s", hipGetErrorString(r));
-  return PKV_OK;
+// Launch `kernel`; with marks, through hipExtLaunchKernel, whose start and
+// stop events the dispatch itself records as the kernel starts and ends.
+template <typename... KArgs, typename... Args>
+void launch_marked(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t lds, hipStream_t st,
+                   hipEvent_t before, hipEvent_t after, Args... args) {
+  if (before)
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, st, before, after, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
 }
 
 int check_launch(const char* what) {
@@ -1254,25 +1259,25 @@ int launch(const LaunchArgs& a) {
       const size_t lds = (size_t)(2 * a.num_seqs + 1) * sizeof(int32_t);
       const int32_t groups = a.plan.workers / a.plan.gs;
       const dim3 grid((uint32_t)(a.plan.workers / kBWaves));
-      int rc = record_mark(a.mark_before, a.stream);
-      if (rc) return rc;
       if (a.k_new)
-        hipLaunchKernelGGL((decode_balanced_kernel<D, B, G, true>), grid, dim3(kBThreads), lds,
-                           a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
-                           (const uint16_t*)a.v_cache, a.block_tables, a.width, a.context_lens,
-                           (uint16_t*)a.out, a.meta, a.part_ml, a.part_o, a.num_seqs,
-                           a.num_kv_heads, a.num_blocks, a.max_context_len, groups, a.plan.gs,
-                           a.qscale, (const uint16_t*)a.k_new, (const uint16_t*)a.v_new,
-                           (uint16_t*)a.k_cache, (uint16_t*)a.v_cache);
+        launch_marked(decode_balanced_kernel<D, B, G, true>, grid, dim3(kBThreads),
+                      (uint32_t)lds, a.stream, a.mark_before, a.mark_after,
+                      (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
+                      (const uint16_t*)a.v_cache, a.block_tables, a.width, a.context_lens,
+                      (uint16_t*)a.out, a.meta, a.part_ml, a.part_o, a.num_seqs, a.num_kv_heads,
+                      a.num_blocks, a.max_context_len, groups, a.plan.gs, a.qscale,
+                      (const uint16_t*)a.k_new, (const uint16_t*)a.v_new, (uint16_t*)a.k_cache,
+                      (uint16_t*)a.v_cache);
       else
-        hipLaunchKernelGGL((decode_balanced_kernel<D, B, G, false>), grid, dim3(kBThreads), lds,
-                           a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
-                           (const uint16_t*)a.v_cache, a.block_tables, a.width, a.context_lens,
-                           (uint16_t*)a.out, a.meta, a.part_ml, a.part_o, a.num_seqs,
-                           a.num_kv_heads, a.num_blocks, a.max_context_len, groups, a.plan.gs,
-                           a.qscale, nullptr, nullptr, nullptr, nullptr);
-      rc = check_launch("decode_balanced");
-      if (!rc) rc = record_mark(a.mark_after, a.stream);
+        launch_marked(decode_balanced_kernel<D, B, G, false>, grid, dim3(kBThreads),
+                      (uint32_t)lds, a.stream, a.mark_before, a.mark_after,
+                      (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
+                      (const uint16_t*)a.v_cache, a.block_tables, a.width, a.context_lens,
+                      (uint16_t*)a.out, a.meta, a.part_ml, a.part_o, a.num_seqs, a.num_kv_heads,
+                      a.num_blocks, a.max_context_len, groups, a.plan.gs, a.qscale,
+                      (const uint16_t*)nullptr, (const uint16_t*)nullptr, (uint16_t*)nullptr,
+                      (uint16_t*)nullptr);
+      int rc = check_launch("decode_balanced");
       if (rc) return rc;
       const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * G;
       hipLaunchKernelGGL((decode_balanced_reduce_kernel<D, G>),
@@ -1285,25 +1290,22 @@ int launch(const LaunchArgs& a) {
   }
   const int64_t grid = (int64_t)a.num_seqs * a.num_kv_heads * a.plan.parts;
   if (grid > INT32_MAX) return pkv__fail(PKV_EINVAL, "decode grid too large");
-  int rc = record_mark(a.mark_before, a.stream);
-  if (rc) return rc;
   if constexpr (E::bytes == 2) {
-    hipLaunchKernelGGL((decode_partition_mfma_kernel<D, B, G>), dim3((uint32_t)grid),
-                       dim3(kThreads), 0, a.stream, (const uint16_t*)a.q,
-                       (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.block_tables,
-                       a.width, a.context_lens, (uint16_t*)a.out, a.part_ml, a.part_o,
-                       a.num_seqs, a.num_kv_heads, a.num_blocks, a.plan.parts, a.plan.ps,
-                       a.max_context_len, a.qscale);
+    launch_marked(decode_partition_mfma_kernel<D, B, G>, dim3((uint32_t)grid), dim3(kThreads), 0u,
+                  a.stream, a.mark_before, a.mark_after, (const uint16_t*)a.q,
+                  (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.block_tables, a.width,
+                  a.context_lens, (uint16_t*)a.out, a.part_ml, a.part_o, a.num_seqs,
+                  a.num_kv_heads, a.num_blocks, a.plan.parts, a.plan.ps, a.max_context_len,
+                  a.qscale);
   } else {
-    hipLaunchKernelGGL((decode_partition_valu_kernel<E, D, B, G>), dim3((uint32_t)grid),
-                       dim3(kThreads), 0, a.stream, (const typename E::raw*)a.q,
-                       (const uint4*)a.k_cache, (const uint4*)a.v_cache, a.block_tables,
-                       a.width, a.context_lens, (typename E::raw*)a.out, a.part_ml, a.part_o,
-                       a.num_seqs, a.num_kv_heads, a.num_blocks, a.plan.parts, a.plan.ps,
-                       a.max_context_len, a.qscale);
+    launch_marked(decode_partition_valu_kernel<E, D, B, G>, dim3((uint32_t)grid), dim3(kThreads),
+                  0u, a.stream, a.mark_before, a.mark_after, (const typename E::raw*)a.q,
+                  (const uint4*)a.k_cache, (const uint4*)a.v_cache, a.block_tables, a.width,
+                  a.context_lens, (typename E::raw*)a.out, a.part_ml, a.part_o, a.num_seqs,
+                  a.num_kv_heads, a.num_blocks, a.plan.parts, a.plan.ps, a.max_context_len,
+                  a.qscale);
   }
-  rc = check_launch("decode_partition");
-  if (!rc) rc = record_mark(a.mark_after, a.stream);
+  int rc = check_launch("decode_partition");
   if (rc) return rc;
   if (a.plan.parts > 1) {
     hipLaunchKernelGGL((decode_reduce_kernel<E, D>), dim3((uint32_t)(a.num_seqs * a.num_q_heads)),

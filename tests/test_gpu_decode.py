@@ -324,8 +324,8 @@ def test_balanced_workspace_reused_across_calls():
 
 @pytest.mark.parametrize("ps", [AUTO, 64])
 def test_marked_events_bracket_the_first_kernel(ps):
-    """pkv_decode_mark_next_call: the next call records the events right
-    around its first kernel only (inside the call's own span), once; a call
+    """pkv_decode_mark_next_call: the next call's first kernel carries the
+    events as its start and stop (inside the call's own span), once; a call
     that fails clears the pair; outputs do not change."""
     q, kc, vc, tables, ctx, scale = _small_case("bf16", 128, 16, 4, 13,
                                                 lens=[4096, 3000, 2049, 1000, 777, 100])
