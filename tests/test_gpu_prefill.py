@@ -83,6 +83,28 @@ def test_small_cases_every_element(case):
     print("max_abs/max_rel", check_close(got, ref, "bf16"))
 
 
+PREFILL_INSTANCES = [(D, G, B) for D in (64, 128) for G in (1, 2, 4, 8, 16) for B in (8, 16, 32)]
+
+
+@pytest.mark.parametrize("inst", PREFILL_INSTANCES, ids=lambda x: "-".join(map(str, x)))
+def test_every_instance_all_elements(inst):
+    """Every built (head_dim, GQA group) instance at every block size: a
+    sequence with a cached prefix and a q-tile boundary, one without a prefix,
+    and one with a single new token."""
+    D, G, B = inst
+    hkv = 2
+    rows = 128 // G  # new tokens per workgroup
+    lens = [150 + rows, rows + 3, 77]
+    news = [rows + 1, rows + 3, 1]
+    print(f"prefill instance D={D} G={G} B={B}", flush=True)
+    rng = np.random.default_rng(D * 1000 + G * 10 + B)
+    q, kc, vc, tables, ctx, qsl = _case(rng, lens, news, hkv * G, hkv, D, B)
+    scale = 1.0 / math.sqrt(D)
+    got = _run(q, kc, vc, tables, ctx, qsl, scale)
+    ref = paged_attention_prefill(q, kc, vc, tables, ctx, qsl, scale, "bf16")
+    check_close(got, ref, "bf16")
+
+
 def test_one_new_token_per_sequence_matches_decode():
     rng = np.random.default_rng(41)
     lens = [1, 15, 16, 17, 200, 1000]
