@@ -72,6 +72,34 @@ def test_fused_equals_write_then_decode(lens, hq, hkv, D, B):
     check_close(host(o2), paged_attention_decode(q, ek, ev, tables, ctx, scale, "bf16"), "bf16")
 
 
+@pytest.mark.parametrize("inst", [(D, B, G) for D in (64, 128) for B in (8, 16, 32)
+                                  for G in (1, 2, 4, 8)], ids=lambda x: "-".join(map(str, x)))
+def test_every_fused_instance(inst):
+    """Every built (head_dim, block size, GQA group) instance of the fused
+    launch: caches and output bit for bit as write then decode, and within
+    the tolerance of the oracle."""
+    D, B, G = inst
+    lens, hkv = [1, B + 1, 200, 513], 2
+    print(f"fused instance D={D} B={B} G={G}", flush=True)
+    rng = np.random.default_rng(D * 100 + B * 10 + G)
+    kc, vc, tables, ctx, slots, nk, nv, q = _state(rng, lens, hkv * G, hkv, D, B)
+    scale = 1.0 / np.sqrt(D)
+    mx = int(ctx.max())
+    k1, v1 = dev(kc), dev(vc)
+    o1 = torch.empty_like(dev(q))
+    pkv.paged_kv_write(dev(nk), dev(nv), dev(slots), k1, v1)
+    pkv.paged_attention_decode(o1, dev(q), k1, v1, dev(tables), dev(ctx), scale, mx)
+    k2, v2 = dev(kc), dev(vc)
+    o2 = torch.empty_like(dev(q))
+    pkv.paged_attention_decode_append(o2, dev(q), dev(nk), dev(nv), k2, v2, dev(tables), dev(ctx),
+                                      scale, mx)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(k1), host(k2)) and np.array_equal(host(v1), host(v2))
+    assert np.array_equal(host(o1), host(o2))
+    ek, ev = paged_kv_write(nk, nv, slots, kc, vc)
+    check_close(host(o2), paged_attention_decode(q, ek, ev, tables, ctx, scale, "bf16"), "bf16")
+
+
 def test_full_size_llama_layer():
     w = datagen.decode_inputs(2)
     sh = w.shape
