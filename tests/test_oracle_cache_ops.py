@@ -53,6 +53,20 @@ def test_copy_blocks_snapshot_and_bits():
         assert np.array_equal(kc2[b], kc[b]) and np.array_equal(vc2[b], vc[b])
 
 
+def test_copy_blocks_reads_sources_as_before_the_call():
+    """The oracle's copy is a batch: a destination takes its source's contents
+    from before the call even when an earlier pair wrote that source (the
+    library's contract excludes such chains, and pkv_validate_copy refuses
+    them; this pins only the oracle's own definition)."""
+    rng = np.random.default_rng(9)
+    kc = bf16_from_f32(rng.standard_normal((6, 2, 4, 3)).astype(np.float32))
+    vc = bf16_from_f32(rng.standard_normal((6, 2, 4, 3)).astype(np.float32))
+    kc2, vc2 = copy_blocks(kc, vc, [(1, 3), (3, 5)])
+    assert np.array_equal(kc2[3], kc[1]) and np.array_equal(vc2[3], vc[1])
+    assert np.array_equal(kc2[5], kc[3]) and np.array_equal(vc2[5], vc[3])
+    assert not np.array_equal(kc[3], kc[1])
+
+
 def test_cow_flow_carries_prefix_before_divergent_write():
     """Page 1 section 4: the copy carries the shared prefix into the fresh
     block, then the divergent token lands in it; the sibling is untouched."""
