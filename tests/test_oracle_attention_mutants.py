@@ -131,7 +131,7 @@ def test_mutant_fails_a_pin(name, monkeypatch):
     for pin, call in _pins():
         try:
             call()
-        except Exception as e:  # an assertion, or an error the mistake provokes
+        except (Exception, pytest.fail.Exception) as e:  # a failed check or a provoked error
             failed.append((pin, type(e).__name__))
     print(name, "fails", failed[:6], f"({len(failed)} pins)")
     assert failed, f"mutant '{name}' passes every attention and cache-op pin"

@@ -107,7 +107,7 @@ def test_mutant_fails_a_pin(name, golden_dir, monkeypatch):
     for pin, call in _pin_calls(golden_dir):
         try:
             call()
-        except Exception as e:  # an assertion, or an error the mistake provokes
+        except (Exception, pytest.fail.Exception) as e:  # a failed check or a provoked error
             failed.append((pin, type(e).__name__))
     print(name, "fails", failed)
     assert failed, f"mutant '{name}' passes every prefix-cache pin"
